@@ -1,0 +1,130 @@
+"""CPU oracle for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
+(``exact_io_aware_13_amd``) never imports it, and the two share no code.
+
+Contents
+--------
+* ``attention_f64`` / ``attention_rows_f64``: ctypes wrappers around the plain
+  C oracle in ``fa_ref.c`` (fp64, one row at a time, OpenMP over rows).  This
+  is the definition the method must reproduce: ordinary softmax attention with
+  the causal rule of "Flash Attention, tiled: exact attention without the T x T
+  HBM matrix" (section "Ordinary causal attention").
+* ``widen_bf16``: exact widening of bf16 bit patterns to float64, so that the
+  oracle consumes the very values the GPU receives.
+* ``online`` (submodule): the online-softmax recurrence, tile by tile, used to
+  check that the recurrence and the definition agree.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_ref.c")
+_LIB = os.path.join(_HERE, "libfa_ref.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``fa_ref.c`` into ``libfa_ref.so`` with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-shared", "-fPIC", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.fa_ref_fwd_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
+                                       ctypes.c_double]
+        lib.fa_ref_fwd_f64.restype = ctypes.c_int
+        lib.fa_ref_fwd_rows_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
+                                            ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64,
+                                            dp, dp]
+        lib.fa_ref_fwd_rows_f64.restype = ctypes.c_int
+        lib.fa_ref_num_threads.argtypes = []
+        lib.fa_ref_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (a bf16 is the top half of an fp32)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _as_f64(x) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return widen_bf16(x)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _check4(q, k, v):
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one (B, H, T, d) shape; got {q.shape}, {k.shape}, {v.shape}")
+
+
+def attention_f64(q, k, v, causal: bool, scale: float):
+    """Exact attention forward over every row.
+
+    ``q, k, v``: (B, H, T, d) arrays, either float64/float32 values or uint16
+    bf16 bit patterns (widened exactly).  Returns ``(o, lse)`` as float64 with
+    shapes (B, H, T, d) and (B, H, T); ``lse`` is in natural-log units.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    _check4(q, k, v)
+    B, H, T, d = q.shape
+    o = np.empty((B, H, T, d), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    rc = _load().fa_ref_fwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                B, H, T, d, int(bool(causal)), float(scale))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd_f64 failed with code {rc}")
+    return o, lse
+
+
+def attention_rows_f64(q, k, v, causal: bool, scale: float, rows):
+    """Exact attention forward for selected rows only.
+
+    ``rows`` holds flat row indices ``(b*H + h)*T + i``.  Returns
+    ``(o_rows, lse_rows)`` with shapes (n, d) and (n,).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    _check4(q, k, v)
+    B, H, T, d = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().fa_ref_fwd_rows_f64(_dptr(q), _dptr(k), _dptr(v), B, H, T, d,
+                                     int(bool(causal)), float(scale),
+                                     rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                     _dptr(o), _dptr(lse))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd_rows_f64 failed with code {rc}")
+    return o, lse
+
+
+def num_threads() -> int:
+    """OpenMP threads the C oracle uses (OMP_NUM_THREADS, else all host cores)."""
+    return int(_load().fa_ref_num_threads())
