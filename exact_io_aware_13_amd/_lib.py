@@ -1,0 +1,125 @@
+"""ctypes binding of ``libfa.so`` (the C ABI in ``include/fa.h``).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels.  torch supplies device memory and the current HIP stream.  If the
+library has not been built, loading fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+# fa_status codes, as in include/fa.h
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEAD_DIM = 3
+FA_ERR_SCALE = 4
+FA_ERR_ALIGN = 5
+FA_ERR_OVERFLOW = 6
+FA_ERR_HIP = 7
+FA_ERR_ARG = 8
+
+EXPORTED = ("fa_fwd", "fa_status_string", "fa_hip_error_string")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa_fwd failed with status {status}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load ``libfa.so`` (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python exact_io_aware_13_amd/build.py) first")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
+        lib.fa_fwd.restype = ctypes.c_int
+        lib.fa_status_string.argtypes = [ctypes.c_int]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_hip_error_string.argtypes = []
+        lib.fa_hip_error_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+               B: int, H: int, T: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Call ``fa_fwd`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, T, d, int(causal),
+                             float(scale), stream))
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        msg = status_string(status)
+        if status == FA_ERR_HIP:
+            msg += f" ({load().fa_hip_error_string().decode()})"
+        raise FAError(status, msg)
+
+
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must have shape (B, H, T, d), got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None) -> None:
+    """Exact attention forward into caller buffers ``o`` (bf16, like q) and ``lse`` (fp32, (B,H,T))."""
+    import torch
+    _check_tensors(q, k, v)
+    B, H, T, d = q.shape
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q on q's device")
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, T) on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, T, d, int(bool(causal)), float(scale), stream))
+
+
+def fwd(q, k, v, causal: bool, scale: float | None = None):
+    """Exact attention forward; returns ``(o, lse)``.
+
+    ``q, k, v``: contiguous bf16 GPU tensors of shape (B, H, T, d), d in {64, 128}.
+    ``scale`` defaults to 1/sqrt(d).  ``o`` is bf16 like ``q``; ``lse`` is
+    float32 (B, H, T) in natural-log units.
+    """
+    import torch
+    _check_tensors(q, k, v)
+    B, H, T, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    fwd_out(q, k, v, o, lse, causal, scale)
+    return o, lse

@@ -1,0 +1,54 @@
+"""Build the gfx950 HIP library ``libfa.so`` in-tree with hipcc.
+
+The library exports the C ABI declared in ``include/fa.h``.  Flags: gfx950
+only, -O3, and packed-fp32 instructions disabled in the device pass
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass prints a
+harmless notice that it does not know that feature.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfa.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def compile_flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE]
+
+
+def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = True) -> str:
+    """Compile ``csrc/fa_fwd.hip`` into ``libfa.so``; returns the library path."""
+    out = out or LIB
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+        return out
+    cmd = [hipcc()] + compile_flags() + list(extra or []) + ["-shared", "-o", out + ".tmp", SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{msg}")
+    if msg.strip() and not quiet:
+        print(msg, file=sys.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(force=True, quiet=False))

@@ -1,0 +1,87 @@
+/*
+ * fa.h -- C ABI of the exact attention forward for MI355X (gfx950).
+ *
+ * One operation, the exact attention forward of one or more heads:
+ *
+ *   O[b,h,i,:] = sum_{j visible to i} softmax_j(scale * q_i . k_j) * v_j
+ *   lse[b,h,i] = ln sum_{j visible to i} exp(scale * q_i . k_j)
+ *
+ * with "visible" meaning every key j < T, or, when causal, every key j <= i.
+ * The problem statement -- (B, H, T, d) tensors, the score matrix scaled by
+ * 1/sqrt(d) by default, future keys masked to -inf before the softmax -- is
+ * the one given on "Flash Attention, tiled: exact attention without the T x T
+ * HBM matrix", section "Ordinary causal attention".  The computation is the
+ * tiled online-softmax forward of the same page ("From the example to tiled
+ * GPU work") and of "FlashAttention: the IO-aware Attention Kernel",
+ * sections 3.2-3.3: the T x T score and probability matrices never reach
+ * memory.  The per-row log-sum-exp is the extra per-row scalar of
+ * "FlashAttention and Fused Kernels: Attention Without the n x n Matrix",
+ * Step 4, returned in natural-log units, so that P_ij = exp(s_ij - lse_i).
+ *
+ * All entry points are plain C: pointers, sizes and a HIP stream handle.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    FA_ERR_SHAPE = 2,     /* B, H or T < 1                                       */
+    FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
+    FA_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
+    FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte   */
+    FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid */
+    FA_ERR_HIP = 7,       /* the kernel launch failed; see fa_hip_error_string()  */
+    FA_ERR_ARG = 8        /* causal not 0/1, or an output overlaps an input       */
+} fa_status;
+
+/*
+ * fa_fwd -- exact attention forward, enqueued on `stream`.
+ *
+ * q, k, v : device pointers to bf16 tensors of shape [B][H][T][d], dense
+ *           row-major (d fastest), 16-byte aligned.  Read only.
+ * o       : device pointer, bf16 [B][H][T][d], same layout; written with
+ *           round-to-nearest-even from the fp32 result.
+ * lse     : device pointer, fp32 [B][H][T]; natural-log log-sum-exp of the
+ *           visible scaled scores of each row.
+ * B, H, T : batch, heads, sequence length (queries and keys alike), >= 1.
+ * d       : head size, 64 or 128.
+ * causal  : 1 = key j visible to query i iff j <= i; 0 = every key visible.
+ * scale   : multiplies q.k; any finite value (callers usually pass
+ *           1/sqrt(d)); 0 gives uniform weights.
+ * stream  : HIP stream to enqueue on; NULL means the default stream.
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library
+ * allocates no memory, keeps no per-call state and is reentrant; o and lse
+ * must not overlap q, k or v.
+ *
+ * Errors: every argument is validated before any HIP call.  On a validation
+ * failure nothing is launched and the matching FA_ERR_* code is returned.
+ * FA_ERR_HIP means the launch was rejected by the runtime; the message is
+ * available from fa_hip_error_string() on the same thread.  FA_OK means the
+ * work was enqueued; completion is observed by synchronising the stream.
+ * Unsupported shapes are rejected, never redirected to another algorithm.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v,
+                 void* o, float* lse,
+                 int64_t B, int64_t H, int64_t T, int64_t d,
+                 int causal, float scale, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(fa_status status);
+
+/* Text of the last HIP error seen by fa_fwd on the calling thread, or "" */
+const char* fa_hip_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Both sides consume the same seeded bf16 bits.  Tolerances (O: max-abs 1e-2,
+relative L2 5e-3; lse: max-abs 1e-3) are the ones the target states for bf16
+inputs against an fp64 oracle.  Small and medium workloads are compared on every
+row; the two long workloads are compared on seeded sample rows plus closed forms
+that hold on every row at full size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_13_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+O_MAX_ABS = 1e-2
+O_REL_L2 = 5e-3
+LSE_MAX_ABS = 1e-3
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_io_aware_13_amd as fa
+    fa.load()   # raises when the HIP library is missing: no fallback
+    oracle.build(force=False)
+    return fa
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+def bf16_to_f64(t):
+    import torch
+    return oracle.widen_bf16(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def run_gpu(fa, qb, kb, vb, causal, scale):
+    import torch
+    o, lse = fa.fwd(to_dev(qb), to_dev(kb), to_dev(vb), causal, float(scale))
+    torch.cuda.synchronize()
+    return bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def bf16_round_f64(x):
+    return oracle.widen_bf16(wl.f32_to_bf16_bits(x.astype(np.float32)))
+
+
+def check(o, o_ref, lse, lse_ref, label):
+    err = np.abs(o - o_ref)
+    max_abs = float(err.max())
+    rel_l2 = float(np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref))
+    lse_abs = float(np.abs(lse - lse_ref).max())
+    floor = float(np.abs(bf16_round_f64(o_ref) - o_ref).max())
+    say(f"[{label}] O max-abs {max_abs:.3e} (bf16 storage floor {floor:.3e}) rel-L2 {rel_l2:.3e} "
+        f"lse max-abs {lse_abs:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert max_abs <= O_MAX_ABS, (label, max_abs)
+    assert rel_l2 <= O_REL_L2, (label, rel_l2)
+    assert lse_abs <= LSE_MAX_ABS, (label, lse_abs)
+    return max_abs, rel_l2, lse_abs
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3nc", "c3c"])
+def test_workload_every_row(fa, key):
+    w = wl.BY_KEY[key]
+    say(f"case {key}: {w.title}")
+    qb, kb, vb = wl.workload_inputs(w)
+    scale = np.float32(w.scale)
+    o, lse = run_gpu(fa, qb, kb, vb, w.causal, scale)
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, w.causal, float(scale))
+    check(o, o_ref, lse, lse_ref, key)
+
+
+def _heads_slice(bits, heads, B, H):
+    flat = bits.reshape(B * H, *bits.shape[2:])
+    return flat[heads][None]
+
+
+def _sampled_parity(fa, w, q_mask=None):
+    qb, kb, vb = wl.workload_inputs(w)
+    scale = np.float32(w.scale)
+    o, lse = run_gpu(fa, qb, kb, vb, w.causal, scale)
+    rows = wl.sample_rows(w, q_mask=q_mask)
+    heads = np.unique(rows // w.T)
+    # the oracle sees only the sampled heads (row indices remapped into the slice)
+    local = np.searchsorted(heads, rows // w.T) * w.T + rows % w.T
+    qs, ks, vs = (_heads_slice(x, heads, w.B, w.H) for x in (qb, kb, vb))
+    o_ref, lse_ref = oracle.attention_rows_f64(qs, ks, vs, w.causal, float(scale), local)
+    o_rows = o.reshape(-1, w.d)[rows]
+    lse_rows = lse.reshape(-1)[rows]
+    check(o_rows, o_ref, lse_rows, lse_ref, f"{w.key} {len(rows)} sampled rows")
+    return o, lse, qb, kb, vb
+
+
+def test_workload_c4_sampled_rows(fa):
+    w = wl.BY_KEY["c4"]
+    say(f"case c4: {w.title}")
+    _sampled_parity(fa, w)
+
+
+def test_workload_c5_sampled_rows_spiky(fa):
+    w = wl.BY_KEY["c5"]
+    say(f"case c5: {w.title}")
+    q_mask, k_mask = wl.spike_masks(w.shape, w.seed)
+    o, lse, *_ = _sampled_parity(fa, w, q_mask=q_mask)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------------------
+# Ragged and small shapes, both head sizes, both masks
+# ---------------------------------------------------------------------------
+
+EDGE = [(1, 1, 1), (1, 1, 3), (1, 1, 4), (2, 1, 63), (1, 2, 64), (1, 1, 65), (1, 3, 127), (2, 2, 128),
+        (1, 1, 129), (1, 2, 200), (1, 1, 1000), (1, 1, 4097)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,T", EDGE, ids=lambda x: str(x))
+def test_edge_shapes(fa, B, H, T, d, causal):
+    say(f"case edge B={B} H={H} T={T} d={d} causal={causal}")
+    qb, kb, vb = wl.draw_bf16((B, H, T, d), seed=1000 + T + d + int(causal))
+    scale = np.float32(1.0 / math.sqrt(d))
+    o, lse = run_gpu(fa, qb, kb, vb, causal, scale)
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, causal, float(scale))
+    check(o, o_ref, lse, lse_ref, f"edge {B}x{H}x{T}x{d} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0625, 0.5, 2.0])
+def test_other_scales(fa, scale):
+    say(f"case scale={scale}")
+    qb, kb, vb = wl.draw_bf16((1, 2, 300, 64), seed=77)
+    for causal in (True, False):
+        o, lse = run_gpu(fa, qb, kb, vb, causal, np.float32(scale))
+        o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, causal, float(np.float32(scale)))
+        check(o, o_ref, lse, lse_ref, f"scale {scale} causal={causal}")
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked examples, run on the GPU
+# ---------------------------------------------------------------------------
+
+def _embed(rows, d):
+    rows = np.asarray(rows, dtype=np.float32)
+    out = np.zeros((1, 1, rows.shape[0], d), dtype=np.float32)
+    out[0, 0, :, :rows.shape[1]] = rows
+    return wl.f32_to_bf16_bits(out)
+
+
+def test_w1_three_token_example(fa):
+    """joelfernandes.org 'A three-token example', zero-padded to d = 64."""
+    import pins
+    g = pins.golden("w1_three_token_causal.json")
+    for d in (64, 128):
+        qb, kb, vb = _embed(g["q"], d), _embed(g["k"], d), _embed(g["v"], d)
+        o, lse = run_gpu(fa, qb, kb, vb, True, np.float32(1.0 / math.sqrt(2.0)))
+        exact = np.array([[10.0, 0.0], [5.0, 10.0], [40.0 / 3.0, 50.0 / 3.0]])
+        assert np.array_equal(o[0, 0, :, :2], bf16_round_f64(exact)), o[0, 0, :, :2]
+        assert np.all(o[0, 0, :, 2:] == 0.0)
+        pins._printed(o[0, 0, :, :2], g["Y"], 1)   # bf16 of 13.333 is 13.3125
+        assert np.allclose(lse[0, 0], [0.0, math.log(2), math.log(3)], atol=1e-6, rtol=0)
+
+
+def test_w2_four_scores_example(fa):
+    """vidyal.ai Step 2: scores [2, 1, 4, 3], values [10, 20, 30, 40] -> 30.3054."""
+    import pins
+    g = pins.golden("w2_four_scores.json")
+    s = np.asarray(g["scores"]); vals = np.asarray(g["values"])
+    q = np.zeros((4, 1)); q[:, 0] = 8.0
+    k = s[:, None]; v = vals[:, None]
+    o, lse = run_gpu(fa, _embed(q, 64), _embed(k, 64), _embed(v, 64), True, np.float32(0.125))
+    assert o[0, 0, 3, 0] == bf16_round_f64(np.array([g["output"]]))[0]   # 30.3054 -> 30.25 in bf16
+    assert o[0, 0, 0, 0] == 10.0
+    assert abs(lse[0, 0, 3] - (4.0 + math.log(g["combine"]["denominator"]))) <= 5e-4
+    assert abs(lse[0, 0, 0] - 2.0) <= 1e-6
+
+
+def test_w4_code_example(fa):
+    """inference-learning-path section 4 inputs (bf16-rounded), non-causal, scale 1/2."""
+    import pins
+    g = pins.golden("w4_online_softmax_code.json")
+    K = np.asarray(g["K"]); T = K.shape[0]
+    q = np.tile(np.asarray(g["q"]), (T, 1))
+    qb, kb, vb = _embed(q, 64), _embed(K, 64), _embed(g["V"], 64)
+    o, lse = run_gpu(fa, qb, kb, vb, False, np.float32(g["scale"]))
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, False, g["scale"])
+    check(o, o_ref, lse, lse_ref, "w4")
+    # the unrounded inputs give the printed values; bf16 inputs stay within 1e-2 of them
+    assert np.max(np.abs(o[0, 0, :, :4] - np.asarray(g["output"]))) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# Closed forms at full size (every row, no O(T^2) oracle)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["c4", "c5"])
+def test_zero_queries_running_mean_full_size(fa, key):
+    """Q = 0: causal O_i is the mean of V_0..V_i and lse_i = ln(i + 1), on every row."""
+    w = wl.BY_KEY[key]
+    say(f"case Q=0 closed form at {w.shape}")
+    _, kb, vb = wl.workload_inputs(w) if key == "c4" else wl.draw_bf16(w.shape, w.seed, False)
+    qb = np.zeros_like(kb)
+    o, lse = run_gpu(fa, qb, kb, vb, True, np.float32(w.scale))
+    n = np.arange(1, w.T + 1, dtype=np.float64)
+    heads = range(w.B * w.H) if key == "c4" else range(0, w.B * w.H, 4)
+    vflat = vb.reshape(w.B * w.H, w.T, w.d)
+    oflat = o.reshape(w.B * w.H, w.T, w.d)
+    worst = 0.0
+    for bh in heads:
+        ref = np.cumsum(oracle.widen_bf16(vflat[bh]), axis=0) / n[:, None]
+        e = np.abs(oflat[bh] - ref).max()
+        worst = max(worst, e)
+        assert e <= O_MAX_ABS, (bh, e)
+    lse_err = np.abs(lse.reshape(w.B * w.H, w.T) - np.log(n)[None]).max()
+    say(f"[Q=0 {key}] O max-abs {worst:.3e} lse max-abs {lse_err:.3e}")
+    assert lse_err <= LSE_MAX_ABS
+
+
+def test_ones_values_give_ones_full_size(fa):
+    """V = 1: every probability row sums to one, so O = 1 exactly in bf16."""
+    w = wl.BY_KEY["c4"]
+    say(f"case V=1 closed form at {w.shape}")
+    qb, kb, _ = wl.workload_inputs(w)
+    vb = np.full_like(qb, 0x3F80)   # bf16 1.0
+    o, lse = run_gpu(fa, qb, kb, vb, True, np.float32(w.scale))
+    assert np.all(o == 1.0)
+    assert np.all(np.isfinite(lse))
+
+
+def test_causal_row0_closed_form(fa):
+    """Causal row 0 sees only key 0: O_0 = V_0 exactly, lse_0 = scale q_0 . k_0."""
+    w = wl.BY_KEY["c4"]
+    qb, kb, vb = wl.workload_inputs(w)
+    scale = np.float32(w.scale)
+    o, lse = run_gpu(fa, qb, kb, vb, True, scale)
+    v0 = oracle.widen_bf16(vb[:, :, 0])
+    assert np.array_equal(o[:, :, 0], v0)
+    q0 = oracle.widen_bf16(qb[:, :, 0]); k0 = oracle.widen_bf16(kb[:, :, 0])
+    assert np.abs(lse[:, :, 0] - float(scale) * np.sum(q0 * k0, axis=-1)).max() <= LSE_MAX_ABS
+
+
+# ---------------------------------------------------------------------------
+# Execution properties
+# ---------------------------------------------------------------------------
+
+def test_deterministic(fa):
+    """No atomics, fixed reduction order: two runs are bit-identical."""
+    import torch
+    w = wl.BY_KEY["c3c"]
+    qb, kb, vb = wl.workload_inputs(w)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o1, l1 = fa.fwd(q, k, v, True)
+    o2, l2 = fa.fwd(q, k, v, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_side_stream_and_preallocated_outputs(fa):
+    import torch
+    qb, kb, vb = wl.draw_bf16((2, 3, 333, 128), seed=5)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((2, 3, 333), float("nan"), device="cuda:0")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa.fwd_out(q, k, v, o, lse, causal=False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, False, 1.0 / math.sqrt(128))
+    check(bf16_to_f64(o), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref, "side stream")
