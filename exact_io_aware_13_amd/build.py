@@ -1,9 +1,10 @@
 """Build the gfx950 HIP library ``libfa.so`` in-tree with hipcc.
 
 The library exports the C ABI declared in ``include/fa.h``.  Flags: gfx950
-only, -O3, and packed-fp32 instructions disabled in the device pass
-(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass prints a
-harmless notice that it does not know that feature.
+only, -O3, packed-fp32 instructions disabled in the device pass
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass prints a
+harmless notice that it does not know that feature), and ``-fno-honor-nans``:
+inputs must be finite, so max reductions need no NaN canonicalisation.
 """
 from __future__ import annotations
 
@@ -28,8 +29,10 @@ def hipcc() -> str:
 
 
 def compile_flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the score tiles feed VALU work directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE]
 
 

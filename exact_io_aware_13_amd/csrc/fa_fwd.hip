@@ -9,29 +9,41 @@
 // probabilities by V at once, and writes O = o / l and the row log-sum-exp after
 // the last tile.  Score and probability tiles live only in registers.
 //
-// gfx950 mapping (one workgroup = 4 waves of 64 lanes, 128 query rows):
-//   * Each wave owns 32 query rows.  It computes the TRANSPOSED score tile
-//     S^T = K_j Q_i^T with v_mfma_f32_32x32x16_bf16, so that in the accumulator
-//     every lane holds 32 scores of ONE query row (lane % 32) -- half the keys of
-//     the tile, the other half in lane ^ 32.  Row max and row sum are then
-//     in-register reductions plus one exchange between the two lane halves.
-//   * The output is accumulated transposed as well, O^T += V_j^T P^T, whose
-//     B operand is exactly the bf16-converted score accumulator (no LDS round
-//     trip for P), and whose accumulator again keeps one query row per lane, so
-//     the rescale factor of a row is lane-local.
-//   * K_j is staged in LDS row-major; V_j is staged transposed (V^T) with the key
-//     order inside each 16-key group permuted to match the accumulator layout of
-//     S^T, so each MFMA operand is one 16-byte LDS read.  Rows are padded by 16
-//     bytes against bank conflicts.  Two LDS stages: tile j+1 is fetched from
-//     HBM into registers while tile j is computed.
-//   * Causal: whole key tiles above a wave's diagonal are skipped; only tiles
-//     that cross the diagonal (or the ragged end of the sequence) are masked.
+// gfx950 mapping (one workgroup = 4 waves of 64 lanes, 128 query rows, 2
+// workgroups per CU):
+//   * Each wave owns 32 query rows and computes the TRANSPOSED score tile
+//     S^T = K_j Q^T with v_mfma_f32_32x32x16_bf16: in the accumulator every lane
+//     holds 32 scores of ONE query row (lane % 32), the other 32 keys of the
+//     64-key tile sitting in lane ^ 32.  Row max and row sums are in-register
+//     reductions plus one v_permlane32_swap.
+//   * The output is accumulated transposed too, O^T += V_j^T P^T: its B operand
+//     is the bf16-converted score accumulator as it stands (no LDS round trip
+//     for P) and its accumulator again keeps one query row per lane, so a row's
+//     rescale factor is lane-local.
+//   * K_j and V_j are copied HBM -> LDS by buffer_load ... lds (no VGPR
+//     staging), one 16-byte chunk per lane, into row-major tiles whose 16-byte
+//     chunks are XOR-swizzled by row so that both the K operand reads
+//     (ds_read_b128) and the transposed V operand reads (ds_read_b64_tr_b16,
+//     which hands each lane 4 keys of one head-dim column) are free of bank
+//     conflicts.  The buffer descriptor of each tile covers only the rows that
+//     exist, so the ragged end of the sequence reads as zeros.
+//   * Software pipeline per wave: while the exponentials of tile j run on the
+//     VALU, the MFMAs of tile j+1's scores are already in flight, and the row
+//     max of tile j+1 is taken while tile j's PV MFMAs run.  LDS holds two K and
+//     two V tiles; tile j+2's K and tile j+1's V are fetched during iteration j.
+//   * The softmax scale is folded into the exponent (one FMA per score, exp2 with
+//     scale*log2(e)); a negative scale negates Q once instead.
 //   * The max is tracked lazily: a row is rescaled only when its tile maximum
 //     exceeds the running reference by more than 2^8 (in exp2 units), the
 //     conditional rescale described for FlashAttention-4 on "FlashAttention and
 //     Fused Kernels: Attention Without the n x n Matrix" ("Four generations").
-//     Weights exp2(x - m) are then at most 256, exact in fp32 and bf16 range,
-//     and the result is unchanged up to rounding.
+//     Weights exp2(x - m) then stay at most 256, and the result is unchanged up
+//     to rounding.  Two row sums are kept: the fp32 sum of the weights (for the
+//     log-sum-exp) and the sum of their bf16 roundings, which are the weights
+//     the PV product actually used (for O = o / l).
+//   * Causal: key tiles past a wave's last query are skipped; only a wave's
+//     last tile can cross its diagonal or the end of the sequence, and only that
+//     tile runs the masked path.
 //   * Workgroup order: the grid is remapped so that a contiguous range of the
 //     work list lands on one XCD (workgroups are dealt round-robin over the 8
 //     XCDs), keeping one head's K/V in that XCD's L2; within a head the heaviest
@@ -41,13 +53,17 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "fa.h"
 
 namespace {
 
+#define FA_LDS __attribute__((address_space(3)))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -59,89 +75,59 @@ constexpr int kXcds = 8;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: rescale when the max grows by > 2^8
+constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor word 3
 
 template <int D>
-struct Tile {
-    static constexpr int kKStride = D + 8;                   // bf16 per K row in LDS
-    static constexpr int kVStride = kBN + 8;                 // bf16 per V^T row in LDS
-    static constexpr int kKElems = kBN * kKStride;
-    static constexpr int kVElems = D * kVStride;
-    static constexpr int kStage = kKElems + kVElems;         // bf16 per LDS stage
-    static constexpr int kKChunks = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
-    static constexpr int kVKeys = D / 32;                    // V rows per thread (8 d values each)
-    static constexpr int kVKeyGroups = kBN / kVKeys;
+struct Geo {
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+    static constexpr int kTileBytes = kBN * kRowBytes;
+    static constexpr int kLoads = D / 32;             // 1 KB buffer->LDS loads per wave per tile
+    static constexpr int kDSteps = D / 16;            // MFMA k-steps over d for S^T
+    static constexpr int kDBlocks = D / 32;           // 32-row blocks of O^T
+    static constexpr int kLdsBytes = 4 * kTileBytes;  // K slot 0, K slot 1, V slot 0, V slot 1
 };
 
+// XOR swizzle of the 16-byte chunk index within a tile row.  D = 128 (16
+// chunks): the two 2-bit fields of row % 16 swapped; D = 64 (8 chunks): a
+// 3-bit permutation of (row / 2) % 8.  Either way 16 consecutive rows map one
+// logical chunk to 16 (resp. 8 x 2 half-rows of) distinct banks, and 4
+// consecutive rows move a 4-chunk group to 4 distinct bank quarters.
 template <int D>
-struct TileRegs {
-    u32x4 k[Tile<D>::kKChunks];
-    u32x4 v[Tile<D>::kVKeys];
-};
-
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// Position of key `key` (0..63 within a tile) in the transposed V tile: bits 2
-// and 3 swapped.  The S^T accumulator gives lane half h, element e of the
-// 16-key step the key 8*(e/4) + 4*h + e%4; with this permutation those eight
-// keys are contiguous at slot 8*h + e.
-__device__ __forceinline__ int vt_slot(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Fetch K/V tile rows [key0, key0+64) of one head into registers (zeros past T).
-template <int D>
-__device__ __forceinline__ void fetch_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbh,
-                                           const uint16_t* __restrict__ vbh, int key0, int T, int tid) {
-    using TL = Tile<D>;
-    constexpr int kChunksPerRow = D / 8;
-#pragma unroll
-    for (int c = 0; c < TL::kKChunks; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int key = key0 + chunk / kChunksPerRow;
-        const int col = chunk % kChunksPerRow;
-        r.k[c] = key < T ? *reinterpret_cast<const u32x4*>(kbh + (size_t)key * D + col * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int kg = tid % TL::kVKeyGroups;
-    const int dg = tid / TL::kVKeyGroups;
-#pragma unroll
-    for (int e = 0; e < TL::kVKeys; ++e) {
-        const int key = key0 + kg * TL::kVKeys + e;
-        r.v[e] = key < T ? *reinterpret_cast<const u32x4*>(vbh + (size_t)key * D + dg * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
 }
 
-// Registers -> one LDS stage: K row-major, V transposed with the slot permutation.
-template <int D>
-__device__ __forceinline__ void stage_tile(const TileRegs<D>& r, uint16_t* ks, uint16_t* vts, int tid) {
-    using TL = Tile<D>;
-    constexpr int kChunksPerRow = D / 8;
-#pragma unroll
-    for (int c = 0; c < TL::kKChunks; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / kChunksPerRow;
-        const int col = chunk % kChunksPerRow;
-        *reinterpret_cast<u32x4*>(ks + row * TL::kKStride + col * 8) = r.k[c];
-    }
-    const int kg = tid % TL::kVKeyGroups;
-    const int dg = tid / TL::kVKeyGroups;
-    const int slot0 = vt_slot(kg * TL::kVKeys);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint16_t* dst = vts + (dg * 8 + e) * TL::kVStride + slot0;
-        if constexpr (TL::kVKeys == 4) {
-            u32x2 w;
-            w.x = ((r.v[0][e >> 1] >> sh) & 0xffffu) | (((r.v[1][e >> 1] >> sh) & 0xffffu) << 16);
-            w.y = ((r.v[2][e >> 1] >> sh) & 0xffffu) | (((r.v[3][e >> 1] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<u32x2*>(dst) = w;
-        } else {
-            static_assert(TL::kVKeys == 2, "head size must be 64 or 128");
-            const uint32_t w = ((r.v[0][e >> 1] >> sh) & 0xffffu) | (((r.v[1][e >> 1] >> sh) & 0xffffu) << 16);
-            *reinterpret_cast<uint32_t*>(dst) = w;
-        }
-    }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// max / sum of a value and its copy in lane ^ 32 (the other half of the row's keys)
+__device__ __forceinline__ float xhalf_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return as_f32(r[0]) + as_f32(r[1]);
+}
+
+// Max of the 32 raw scores a lane holds, then across the lane pair.
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+    float a0 = max3f(s[0][0], s[0][1], s[0][2]), a1 = max3f(s[0][3], s[0][4], s[0][5]);
+    float a2 = max3f(s[0][6], s[0][7], s[0][8]), a3 = max3f(s[0][9], s[0][10], s[0][11]);
+    float a4 = max3f(s[0][12], s[0][13], s[0][14]), a5 = max3f(s[0][15], s[1][0], s[1][1]);
+    float a6 = max3f(s[1][2], s[1][3], s[1][4]), a7 = max3f(s[1][5], s[1][6], s[1][7]);
+    float a8 = max3f(s[1][8], s[1][9], s[1][10]), a9 = max3f(s[1][11], s[1][12], s[1][13]);
+    float a10 = fmaxf(s[1][14], s[1][15]);
+    float b0 = max3f(a0, a1, a2), b1 = max3f(a3, a4, a5), b2 = max3f(a6, a7, a8), b3 = fmaxf(a9, a10);
+    return xhalf_max(fmaxf(max3f(b0, b1, b2), b3));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -151,20 +137,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+template <int D>
+struct WaveState {
+    f32x16 o[Geo<D>::kDBlocks];   // O^T accumulator: lane holds d-rows of its query
+    float m = -INFINITY;          // running reference max (exp2 units)
+    float l32 = 0.0f;             // sum of fp32 weights
+    float l16 = 0.0f;             // sum of bf16-rounded weights
+};
+
+// Lazily move the reference max to m_new when it grew by more than the threshold.
+template <int D>
+__device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float m_new) {
+    const bool need = m_new > st.m + kRescaleThreshold;
+    if (__any(need)) {
+        const float r = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
+        st.m = need ? m_new : st.m;
+        st.l32 *= r;
+        st.l16 *= r;
+#pragma unroll
+        for (int b = 0; b < Geo<D>::kDBlocks; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.o[b][i] *= r;
+    }
+}
+
+// One workgroup's work; `lds` is the workgroup's Geo<D>::kLdsBytes of LDS.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                   int T, int n_qt, int total, float c /* scale * log2(e) */) {
-    using TL = Tile<D>;
-    constexpr int kDSteps = D / 16;   // MFMA k-steps over the head dimension
-    constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
+__device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                             const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                             float* __restrict__ LSE, int T, int n_qt, int total, float c_in,
+                                             FA_LDS char* const lds) {
+    using G = Geo<D>;
+    FA_LDS char* const kslot[2] = {lds, lds + G::kTileBytes};
+    FA_LDS char* const vslot[2] = {lds + 2 * G::kTileBytes, lds + 3 * G::kTileBytes};
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::kStage];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;   // this lane's query row within the wave
     const int half = lane >> 5;
 
@@ -177,150 +185,245 @@ void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int qt = CAUSAL ? n_qt - 1 - (w % n_qt) : (w % n_qt);
 
     const size_t base = (size_t)bh * (size_t)T * D;
-    const uint16_t* __restrict__ qbh = Q + base;
     const uint16_t* __restrict__ kbh = K + base;
     const uint16_t* __restrict__ vbh = V + base;
+    const uint32_t head_bytes = (uint32_t)T * G::kRowBytes;
 
     const int qw0 = qt * kBM + wave * 32;   // first query row of this wave
     const int qrow = qw0 + col;
-    const bool wave_active = qw0 < T;
-    const int wave_last_key = CAUSAL ? min(qw0 + 31, T - 1) : T - 1;
+    const int n_all = (T + kBN - 1) / kBN;
+    const int kv_end = CAUSAL ? min(T, qt * kBM + kBM) : T;
+    const int n_kt = (kv_end + kBN - 1) / kBN;                       // tiles the workgroup loads
+    const int n_w = qw0 >= T ? 0 : (CAUSAL ? min(n_all, (qw0 + 31) / kBN + 1) : n_all);  // tiles this wave uses
 
-    // Q^T operand: lane holds Q[qrow][16 s + 8 half .. +7].
-    bf16x8 qf[kDSteps];
+    // Per-lane byte offsets of this lane's 16-byte chunk in each tile load, and
+    // the matching LDS destination of the wave's 1 KB block.
+    uint32_t goff[G::kLoads];
 #pragma unroll
-    for (int s = 0; s < kDSteps; ++s) {
-        u32x4 raw = qrow < T ? *reinterpret_cast<const u32x4*>(qbh + (size_t)qrow * D + 16 * s + 8 * half)
-                             : u32x4{0u, 0u, 0u, 0u};
-        qf[s] = __builtin_bit_cast(bf16x8, raw);
+    for (int c = 0; c < G::kLoads; ++c) {
+        const int q = (wave * G::kLoads + c) * 64 + lane;
+        const int r = q / G::kChunks, p = q % G::kChunks;
+        goff[c] = r * G::kRowBytes + 16 * (p ^ swz<D>(r));
+    }
+    auto load_tile = [&] __device__ (const uint16_t* src, int key0, FA_LDS char* slot) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (size_t)key0 * D, (uint32_t)(T - key0) * G::kRowBytes);
+#pragma unroll
+        for (int c = 0; c < G::kLoads; ++c)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(slot + (wave * G::kLoads + c) * 1024), 16,
+                                                     goff[c], 0, 0, 0);
+    };
+
+    // LDS read offsets.  K (A operand of S^T): row = key col, logical chunk 2 s + half.
+    uint32_t koff[G::kDSteps];
+#pragma unroll
+    for (int s = 0; s < G::kDSteps; ++s) koff[s] = col * G::kRowBytes + 16 * ((2 * s + half) ^ swz<D>(col));
+    // V (A operand of O^T, transposed read): in 16-lane group g, lane i fetches 4 d-values of
+    // row 8 e + 4 half + i / 4 (plus 16 per key step) at column 32 db + 16 (g % 2) + 4 (i % 4).
+    uint32_t voff[G::kDBlocks][2];
+    {
+        const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+        for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 8 * e + 4 * half + (i >> 2);
+                const int cc = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+                voff[db][e] = r * G::kRowBytes + 16 * ((cc >> 3) ^ swz<D>(r)) + 2 * (cc & 7);
+            }
     }
 
-    f32x16 oacc[kDBlocks];
-#pragma unroll
-    for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[b][i] = 0.0f;
-    float m = -INFINITY;   // running reference max, log2 units
-    float l32 = 0.0f;      // sum of fp32 weights (for lse)
-    float l16 = 0.0f;      // sum of the bf16-rounded weights fed to the PV product (for O)
+    // Start fetching: K_0, V_0, K_1.
+    load_tile(kbh, 0, kslot[0]);
+    load_tile(vbh, 0, vslot[0]);
+    if (n_kt > 1) load_tile(kbh, kBN, kslot[1]);
 
-    const int kv_end = CAUSAL ? min(T, qt * kBM + kBM) : T;
-    const int n_kt = ceil_div(kv_end, kBN);
+    // Q^T operand (B operand of S^T): lane holds Q[qrow][16 s + 8 half .. +7]; zeros past T.
+    bf16x8 qf[G::kDSteps];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, head_bytes);
+        const uint32_t neg = c_in < 0.0f ? 0x80008000u : 0u;
+#pragma unroll
+        for (int s = 0; s < G::kDSteps; ++s) {
+            u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qrow * G::kRowBytes + 32 * s + 16 * half,
+                                                              0, 0);
+            raw ^= neg;
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    const float c = fabsf(c_in);
 
-    TileRegs<D> tr;
-    fetch_tile<D>(tr, kbh, vbh, 0, T, tid);
-    stage_tile<D>(tr, smem, smem + TL::kKElems, tid);
-    __syncthreads();
+    WaveState<D> st;
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[b][i] = 0.0f;
 
-    for (int j = 0; j < n_kt; ++j) {
-        const uint16_t* ks = smem + (j & 1) * TL::kStage;
-        const uint16_t* vts = ks + TL::kKElems;
-        if (j + 1 < n_kt) fetch_tile<D>(tr, kbh, vbh, (j + 1) * kBN, T, tid);
-
-        const int key0 = j * kBN;
-        if (wave_active && key0 <= wave_last_key) {
-            // S^T = K_j Q^T : two 32-key blocks.
-            f32x16 sacc[2];
+    auto qk = [&] __device__ (FA_LDS const char* ks, f32x16 (&s)[2]) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[b][i] = 0.0f;
+            for (int i = 0; i < 16; ++i) s[b][i] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < kDSteps; ++s) {
+        for (int t = 0; t < G::kDSteps; ++t)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + col) * TL::kKStride +
-                                                                      16 * s + 8 * half);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-                }
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = *(FA_LDS const bf16x8*)(ks + kb * 32 * G::kRowBytes + koff[t]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
             }
-
-            // Scale into exp2 units; mask keys past the diagonal or past T.
-            float x[32];
+    };
+    auto pv = [&] __device__ (FA_LDS const char* vs, const uint32_t (&pk)[16]) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 praw = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[kb * 16 + i] = sacc[kb][i] * c;
-            const bool need_mask = (CAUSAL && key0 + kBN - 1 > qw0) || (key0 + kBN > T);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        const bool hide = (CAUSAL && key > qrow) || key >= T;
-                        x[kb * 16 + i] = hide ? -INFINITY : x[kb * 16 + i];
-                    }
-            }
-
-            // Row max over the tile (in-register, then across the two lane halves).
-            float mt = x[0];
-#pragma unroll
-            for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m, mt);
-            const bool need = m_new > m + kRescaleThreshold;
-            if (__any(need)) {
-                const float r = need ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-                m = need ? m_new : m;
-                l32 *= r;
-                l16 *= r;
-#pragma unroll
-                for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[b][i] *= r;
-            }
-            const float mu = (m == -INFINITY) ? 0.0f : m;
-
-            // Weights, both row sums, bf16 P^T operand.
-            uint32_t pk[16];
-            const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                const float p0 = __builtin_amdgcn_exp2f(x[2 * n] - mu);
-                const float p1 = __builtin_amdgcn_exp2f(x[2 * n + 1] - mu);
-                l32 += p0;
-                l32 += p1;
-                pk[n] = pack_bf16x2(p0, p1);
-                l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, l16, false);
-            }
-
-            // O^T += V_j^T P^T : four 16-key steps.
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const u32x4 praw = {pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]};
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
-#pragma unroll
-                for (int b = 0; b < kDBlocks; ++b) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(vts + (b * 32 + col) * TL::kVStride +
-                                                                      16 * st + 8 * half);
-                    oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[b], 0, 0, 0);
-                }
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][0]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][1]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 araw = {l2[0], l2[1], h2[0], h2[1]};
+                st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, araw), pb, st.o[db],
+                                                                    0, 0, 0);
             }
         }
+    };
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-        if (j + 1 < n_kt)
-            stage_tile<D>(tr, smem + ((j + 1) & 1) * TL::kStage, smem + ((j + 1) & 1) * TL::kStage + TL::kKElems,
-                          tid);
-        __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads have landed
+    __syncthreads();
+
+    // Two score buffers: even steps turn sa into probabilities while sb fills, odd
+    // steps the other way round (a static register renaming, no copies).
+    f32x16 sa[2], sb[2];
+    if (n_w > 0) {
+        qk(kslot[0], sa);
+        if (n_w > 1) st.m = tile_max(sa) * c;
+    }
+
+    // Tiles every wave of the workgroup treats as unmasked, with a successor:
+    // wave 0 has the fewest tiles, and its last one is left to the tail.
+    const int n_w0 = qt * kBM >= T ? 0 : (CAUSAL ? min(n_all, (qt * kBM + 31) / kBN + 1) : n_all);
+    const int n_steady = max(0, n_w0 - 1);
+
+    // Steady tile j (parity P): tile j+1's score MFMAs overlap tile j's
+    // exponentials; tile j+1's max is taken while tile j's PV MFMAs run.
+    auto steady = [&] __device__ (int j, auto parity, f32x16 (&sc)[2], f32x16 (&sn)[2], bool next_steady) {
+        constexpr int P = decltype(parity)::value;   // j % 2
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();   // K_{j+1}, V_j landed; every wave is done with K_j and V_{j-1}
+        if (j + 2 < n_kt) load_tile(kbh, (j + 2) * kBN, kslot[P]);
+        if (j + 1 < n_kt) load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
+        qk(kslot[P ^ 1], sn);
+        uint32_t pk[16];
+        const float mneg = -st.m;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const float x0 = n < 8 ? sc[0][2 * n] : sc[1][2 * n - 16];
+            const float x1 = n < 8 ? sc[0][2 * n + 1] : sc[1][2 * n - 15];
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, mneg));
+            st.l32 += p0;
+            st.l32 += p1;
+            pk[n] = pack_bf16x2(p0, p1);
+        }
+        pv(vslot[P], pk);
+#pragma unroll
+        for (int n = 0; n < 16; ++n)
+            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
+        if (next_steady) maybe_rescale<D>(st, tile_max(sn) * c);
+    };
+
+    // A wave's last tile (parity P): mask keys past its diagonal or past T.
+    auto last = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
+        constexpr int P = decltype(parity)::value;
+        const int key0 = j * kBN;
+        float x[32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const bool vis = key < T && (!CAUSAL || key <= qrow);
+                x[kb * 16 + i] = vis ? sc[kb][i] * c : -INFINITY;
+            }
+        float mt = x[0];
+#pragma unroll
+        for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
+        maybe_rescale<D>(st, fmaxf(st.m, xhalf_max(mt)));
+        const float mu = st.m == -INFINITY ? 0.0f : st.m;
+        uint32_t pk[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const float p0 = __builtin_amdgcn_exp2f(x[2 * n] - mu);
+            const float p1 = __builtin_amdgcn_exp2f(x[2 * n + 1] - mu);
+            st.l32 += p0;
+            st.l32 += p1;
+            pk[n] = pack_bf16x2(p0, p1);
+            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
+        }
+        pv(vslot[P], pk);
+    };
+
+    // Tail tile j (parity P): per-wave steady / last / idle, plus the loads.
+    auto tail = [&] __device__ (int j, auto parity, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+        constexpr int P = decltype(parity)::value;
+        if (j + 1 < n_w) {
+            steady(j, parity, sc, sn, j + 2 < n_w);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (j + 2 < n_kt) load_tile(kbh, (j + 2) * kBN, kslot[P]);
+            if (j + 1 < n_kt) load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
+            if (j + 1 == n_w) last(j, parity, sc);
+        }
+    };
+
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    int j = 0;
+    for (; j + 1 < n_steady; j += 2) {
+        steady(j, Even{}, sa, sb, true);
+        steady(j + 1, Odd{}, sb, sa, true);
+    }
+    // Tiles n_steady_even .. n_kt-1: the odd leftover steady tile and the masked ends.
+    for (; j < n_kt; j += 2) {
+        if (j < n_steady) steady(j, Even{}, sa, sb, true);
+        else tail(j, Even{}, sa, sb);
+        if (j + 1 < n_kt) tail(j + 1, Odd{}, sb, sa);
     }
 
     // Epilogue: O = o / l (bf16, round to nearest even), lse = ln2 * (m + log2 l).
-    l32 += __shfl_xor(l32, 32);
-    l16 += __shfl_xor(l16, 32);
-    if (!wave_active || qrow >= T) return;
+    const float l32 = xhalf_sum(st.l32);
+    const float l16 = xhalf_sum(st.l16);
+    if (n_w == 0) return;
     const float inv = 1.0f / l16;
-    uint16_t* orow = O + base + (size_t)qrow * D;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + base, head_bytes);   // rows past T are dropped
+    const uint32_t orow = (uint32_t)qrow * G::kRowBytes;
 #pragma unroll
-    for (int b = 0; b < kDBlocks; ++b)
+    for (int b = 0; b < G::kDBlocks; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             u32x2 wv;
-            wv.x = pack_bf16x2(oacc[b][4 * g + 0] * inv, oacc[b][4 * g + 1] * inv);
-            wv.y = pack_bf16x2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * g + 4 * half) = wv;
+            wv.x = pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv);
+            wv.y = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
+            __builtin_amdgcn_raw_buffer_store_b64(wv, ro, orow + 2 * (b * 32 + 8 * g + 4 * half), 0, 0);
         }
-    if (half == 0) LSE[(size_t)bh * T + qrow] = kLn2 * (m + __builtin_amdgcn_logf(l32));
+    if (half == 0) {
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)bh * T, (uint32_t)T * 4u);
+        __builtin_amdgcn_raw_buffer_store_b32(as_u32(kLn2 * (st.m + __builtin_amdgcn_logf(l32))), rl,
+                                              (uint32_t)qrow * 4u, 0, 0);
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+                   int T, int n_qt, int total, float c_in /* scale * log2(e) */) {
+    __shared__ __attribute__((aligned(1024))) char smem[Geo<D>::kLdsBytes];
+    fa_fwd_block<D, CAUSAL>(Q, K, V, O, LSE, T, n_qt, total, c_in, (FA_LDS char*)smem);
 }
 
 thread_local char g_hip_error[256] = "";
@@ -360,6 +463,8 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     const int64_t rows = BH * T;
     if (rows > kMax / (2 * d)) return FA_ERR_OVERFLOW;
     if (T > INT32_MAX - 2 * kBM) return FA_ERR_OVERFLOW;
+    // Buffer descriptors address one head: (T + 2 query tiles) rows must fit in 32-bit byte offsets.
+    if ((T + 2 * kBM) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
     const int64_t n_qt = (T + kBM - 1) / kBM;
     if (BH > INT32_MAX / n_qt) return FA_ERR_OVERFLOW;
     const int total = static_cast<int>(BH * n_qt);
