@@ -77,6 +77,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: rescale when the max grows by > 2^8
 constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor word 3
 
+// Waves of one workgroup per SIMD: 1 gives each wave the full 512-entry
+// register file (VGPR + AGPR); 2 halves it and lets two workgroups share a CU.
+#ifndef FA_WAVES_PER_EU
+#define FA_WAVES_PER_EU 2
+#endif
+// 1: a wave keeps the next tile's scores in flight under the current softmax;
+// 0: one score tile at a time (fewer registers; the other wave on the SIMD overlaps).
+#ifndef FA_PIPELINE
+#define FA_PIPELINE 0
+#endif
+
 template <int D>
 struct Geo {
     static constexpr int kRowBytes = D * 2;
@@ -235,7 +246,9 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     // Start fetching: K_0, V_0, K_1.
     load_tile(kbh, 0, kslot[0]);
     load_tile(vbh, 0, vslot[0]);
+#if FA_PIPELINE
     if (n_kt > 1) load_tile(kbh, kBN, kslot[1]);
+#endif
 
     // Q^T operand (B operand of S^T): lane holds Q[qrow][16 s + 8 half .. +7]; zeros past T.
     bf16x8 qf[G::kDSteps];
@@ -297,10 +310,12 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     // Two score buffers: even steps turn sa into probabilities while sb fills, odd
     // steps the other way round (a static register renaming, no copies).
     f32x16 sa[2], sb[2];
+#if FA_PIPELINE
     if (n_w > 0) {
         qk(kslot[0], sa);
         if (n_w > 1) st.m = tile_max(sa) * c;
     }
+#endif
 
     // Tiles every wave of the workgroup treats as unmasked, with a successor:
     // wave 0 has the fewest tiles, and its last one is left to the tail.
@@ -333,6 +348,33 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         for (int n = 0; n < 16; ++n)
             st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
         if (next_steady) maybe_rescale<D>(st, tile_max(sn) * c);
+    };
+
+    // Steady tile j without the in-wave pipeline: scores, max, weights, PV.
+    auto steady_np = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
+        constexpr int P = decltype(parity)::value;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();   // K_j, V_j landed; every wave is done with K_{j-1}, V_{j-1}
+        if (j + 1 < n_kt) {
+            load_tile(kbh, (j + 1) * kBN, kslot[P ^ 1]);
+            load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
+        }
+        qk(kslot[P], sc);
+        maybe_rescale<D>(st, tile_max(sc) * c);
+        uint32_t pk[16];
+        const float mneg = -st.m;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const float x0 = n < 8 ? sc[0][2 * n] : sc[1][2 * n - 16];
+            const float x1 = n < 8 ? sc[0][2 * n + 1] : sc[1][2 * n - 15];
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, mneg));
+            st.l32 += p0;
+            st.l32 += p1;
+            pk[n] = pack_bf16x2(p0, p1);
+            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
+        }
+        pv(vslot[P], pk);
     };
 
     // A wave's last tile (parity P): mask keys past its diagonal or past T.
@@ -382,6 +424,36 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 
     using Even = std::integral_constant<int, 0>;
     using Odd = std::integral_constant<int, 1>;
+#if !FA_PIPELINE
+    // Non-pipelined order: K_j and V_j share a stage; tile j+1 loads during tile j.
+    auto tail_np = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
+        constexpr int P = decltype(parity)::value;
+        if (j + 1 < n_w) {
+            steady_np(j, parity, sc);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (j + 1 < n_kt) {
+                load_tile(kbh, (j + 1) * kBN, kslot[P ^ 1]);
+                load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
+            }
+            if (j + 1 == n_w) {
+                qk(kslot[P], sc);
+                last(j, parity, sc);
+            }
+        }
+    };
+    int j = 0;
+    for (; j + 1 < n_steady; j += 2) {
+        steady_np(j, Even{}, sa);
+        steady_np(j + 1, Odd{}, sa);
+    }
+    for (; j < n_kt; j += 2) {
+        if (j < n_steady) steady_np(j, Even{}, sa);
+        else tail_np(j, Even{}, sa);
+        if (j + 1 < n_kt) tail_np(j + 1, Odd{}, sa);
+    }
+#else
     int j = 0;
     for (; j + 1 < n_steady; j += 2) {
         steady(j, Even{}, sa, sb, true);
@@ -393,6 +465,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         else tail(j, Even{}, sa, sb);
         if (j + 1 < n_kt) tail(j + 1, Odd{}, sb, sa);
     }
+#endif
 
     // Epilogue: O = o / l (bf16, round to nearest even), lse = ln2 * (m + log2 l).
     const float l32 = xhalf_sum(st.l32);
@@ -418,7 +491,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU, FA_WAVES_PER_EU)))
 void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                    int T, int n_qt, int total, float c_in /* scale * log2(e) */) {
