@@ -79,8 +79,9 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"{len(rows)} of {n_rows_total} query rows, evenly spaced over all heads "
-                   f"({row_flops(rows) / 1e9:.1f} GFLOP in {dt:.1f} s, fp64, OpenMP)"),
+        "sample": ((f"all {n_rows_total} query rows (the whole workload)" if len(rows) == n_rows_total else
+                    f"{len(rows)} of {n_rows_total} query rows, evenly spaced over all heads")
+                   + f" ({row_flops(rows) / 1e9:.1f} GFLOP in {dt:.1f} s, fp64, OpenMP)"),
     }
 
 

@@ -33,7 +33,6 @@ def compile_flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # MFMA accumulators in VGPRs: the score tiles feed VALU work directly
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-mllvm", "-amdgpu-sched-strategy=max-ilp",
             "-I", INCLUDE]
 
 

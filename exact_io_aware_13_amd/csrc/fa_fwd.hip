@@ -9,8 +9,8 @@
 // probabilities by V at once, and writes O = o / l and the row log-sum-exp after
 // the last tile.  Score and probability tiles live only in registers.
 //
-// gfx950 mapping (one workgroup = 4 waves of 64 lanes, 128 query rows, 2
-// workgroups per CU):
+// gfx950 mapping: one workgroup of 8 waves (256 query rows) per CU; waves w and
+// w + 4 share SIMD w % 4.
 //   * Each wave owns 32 query rows and computes the TRANSPOSED score tile
 //     S^T = K_j Q^T with v_mfma_f32_32x32x16_bf16: in the accumulator every lane
 //     holds 32 scores of ONE query row (lane % 32), the other 32 keys of the
@@ -20,30 +20,36 @@
 //     is the bf16-converted score accumulator as it stands (no LDS round trip
 //     for P) and its accumulator again keeps one query row per lane, so a row's
 //     rescale factor is lane-local.
+//   * Ping-pong between the two waves of a SIMD.  Waves 0-3 run one phase ahead
+//     of waves 4-7, and a workgroup barrier separates phases, so in every phase
+//     one wave of each SIMD runs a matrix phase (PV of tile j and S^T of tile
+//     j+1: 32 MFMAs) while the other runs a softmax phase (max, exponentials,
+//     row sums of tile j+1: VALU work).  The two kinds of work then co-issue on
+//     the SIMD instead of competing for the same unit.  This is the
+//     producer/consumer overlap of softmax with the matrix products described
+//     for FlashAttention-3 on "FlashAttention and Fused Kernels: Attention
+//     Without the n x n Matrix" ("Four generations"), done here with wave groups
+//     and barriers.
 //   * K_j and V_j are copied HBM -> LDS by buffer_load ... lds (no VGPR
 //     staging), one 16-byte chunk per lane, into row-major tiles whose 16-byte
 //     chunks are XOR-swizzled by row so that both the K operand reads
 //     (ds_read_b128) and the transposed V operand reads (ds_read_b64_tr_b16,
 //     which hands each lane 4 keys of one head-dim column) are free of bank
 //     conflicts.  The buffer descriptor of each tile covers only the rows that
-//     exist, so the ragged end of the sequence reads as zeros.
-//   * Software pipeline per wave: while the exponentials of tile j run on the
-//     VALU, the MFMAs of tile j+1's scores are already in flight, and the row
-//     max of tile j+1 is taken while tile j's PV MFMAs run.  LDS holds two K and
-//     two V tiles; tile j+2's K and tile j+1's V are fetched during iteration j.
+//     exist, so the ragged end of the sequence reads as zeros.  All 8 waves share
+//     each tile; LDS holds two K and two V tiles, fetched two phases ahead.
 //   * The softmax scale is folded into the exponent (one FMA per score, exp2 with
 //     scale*log2(e)); a negative scale negates Q once instead.
 //   * The max is tracked lazily: a row is rescaled only when its tile maximum
 //     exceeds the running reference by more than 2^8 (in exp2 units), the
-//     conditional rescale described for FlashAttention-4 on "FlashAttention and
-//     Fused Kernels: Attention Without the n x n Matrix" ("Four generations").
+//     conditional rescale described for FlashAttention-4 on the same page.
 //     Weights exp2(x - m) then stay at most 256, and the result is unchanged up
 //     to rounding.  Two row sums are kept: the fp32 sum of the weights (for the
 //     log-sum-exp) and the sum of their bf16 roundings, which are the weights
 //     the PV product actually used (for O = o / l).
 //   * Causal: key tiles past a wave's last query are skipped; only a wave's
 //     last tile can cross its diagonal or the end of the sequence, and only that
-//     tile runs the masked path.
+//     tile runs the masked softmax.
 //   * Workgroup order: the grid is remapped so that a contiguous range of the
 //     work list lands on one XCD (workgroups are dealt round-robin over the 8
 //     XCDs), keeping one head's K/V in that XCD's L2; within a head the heaviest
@@ -68,32 +74,35 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;        // query rows per workgroup
+constexpr int kBM = 256;        // query rows per workgroup (8 waves x 32 rows)
 constexpr int kBN = 64;         // keys per K/V tile
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: rescale when the max grows by > 2^8
 constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor word 3
+#ifndef FA_MATRIX_PRIO
+#define FA_MATRIX_PRIO 1
+#endif
+#ifndef FA_ODD_BARRIER
+#define FA_ODD_BARRIER 0
+#endif
+#ifndef FA_SPECULATE
+#define FA_SPECULATE 1
+#endif
+#ifndef FA_FUSED_PVQK
+#define FA_FUSED_PVQK 0
+#endif
 
-// Waves of one workgroup per SIMD: 1 gives each wave the full 512-entry
-// register file (VGPR + AGPR); 2 halves it and lets two workgroups share a CU.
-#ifndef FA_WAVES_PER_EU
-#define FA_WAVES_PER_EU 2
-#endif
-// 1: a wave keeps the next tile's scores in flight under the current softmax;
-// 0: one score tile at a time (fewer registers; the other wave on the SIMD overlaps).
-#ifndef FA_PIPELINE
-#define FA_PIPELINE 0
-#endif
 
 template <int D>
 struct Geo {
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;            // 16-byte chunks per row
     static constexpr int kTileBytes = kBN * kRowBytes;
-    static constexpr int kLoads = D / 32;             // 1 KB buffer->LDS loads per wave per tile
+    static constexpr int kLoads = kTileBytes / 1024 / kWaves;  // 1 KB buffer->LDS loads per wave per tile
     static constexpr int kDSteps = D / 16;            // MFMA k-steps over d for S^T
     static constexpr int kDBlocks = D / 32;           // 32-row blocks of O^T
     static constexpr int kLdsBytes = 4 * kTileBytes;  // K slot 0, K slot 1, V slot 0, V slot 1
@@ -148,6 +157,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Scheduling groups for PV key step S of the fused PV + QK stream: its NB
+// MFMAs, then the LDS reads issued after them (V two steps ahead, a share of K).
+template <int NK, int NB, int K0, int KPS, int S>
+__device__ __forceinline__ void sgb_pv_step() {
+    constexpr int lo = K0 + S * KPS < NK ? K0 + S * KPS : NK;
+    constexpr int hi = K0 + (S + 1) * KPS < NK ? K0 + (S + 1) * KPS : NK;
+    constexpr int reads = (S + 2 < 4 ? 2 * NB : 0) + (hi - lo);
+    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+    if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
+}
+
 template <int D>
 struct WaveState {
     f32x16 o[Geo<D>::kDBlocks];   // O^T accumulator: lane holds d-rows of its query
@@ -172,6 +192,7 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float m_new) {
     }
 }
 
+
 // One workgroup's work; `lds` is the workgroup's Geo<D>::kLdsBytes of LDS.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -184,6 +205,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;   // 0: leading wave group, 1: one phase behind
     const int col = lane & 31;   // this lane's query row within the wave
     const int half = lane >> 5;
 
@@ -207,8 +229,8 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     const int n_kt = (kv_end + kBN - 1) / kBN;                       // tiles the workgroup loads
     const int n_w = qw0 >= T ? 0 : (CAUSAL ? min(n_all, (qw0 + 31) / kBN + 1) : n_all);  // tiles this wave uses
 
-    // Per-lane byte offsets of this lane's 16-byte chunk in each tile load, and
-    // the matching LDS destination of the wave's 1 KB block.
+    // Per-lane byte offsets of this lane's 16-byte chunk in each tile load; the
+    // wave's 1 KB blocks of a tile are contiguous in LDS.
     uint32_t goff[G::kLoads];
 #pragma unroll
     for (int c = 0; c < G::kLoads; ++c) {
@@ -243,12 +265,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             }
     }
 
-    // Start fetching: K_0, V_0, K_1.
-    load_tile(kbh, 0, kslot[0]);
-    load_tile(vbh, 0, vslot[0]);
-#if FA_PIPELINE
-    if (n_kt > 1) load_tile(kbh, kBN, kslot[1]);
-#endif
+    load_tile(kbh, 0, kslot[0]);   // K_0; K_1 and V_0 follow in phase 0
 
     // Q^T operand (B operand of S^T): lane holds Q[qrow][16 s + 8 half .. +7]; zeros past T.
     bf16x8 qf[G::kDSteps];
@@ -270,202 +287,252 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     for (int b = 0; b < G::kDBlocks; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) st.o[b][i] = 0.0f;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
+    // S^T = K_j Q^T.  All K operand reads are written first; the scheduling
+    // barriers then pin a pipeline that keeps kQkAhead reads in flight ahead of
+    // the MFMA that consumes them.
     auto qk = [&] __device__ (FA_LDS const char* ks, f32x16 (&s)[2]) {
+        constexpr int N = 2 * G::kDSteps;
+#ifndef FA_QK_AHEAD
+#define FA_QK_AHEAD 4
+#endif
+        constexpr int kQkAhead = FA_QK_AHEAD;
+        bf16x8 a[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            a[i] = *(FA_LDS const bf16x8*)(ks + (i & 1) * 32 * G::kRowBytes + koff[i >> 1]);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[b][i] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < G::kDSteps; ++t)
+        for (int i = 0; i < N; ++i)
+            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+#ifndef FA_NO_QK_SGB
+        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *(FA_LDS const bf16x8*)(ks + kb * 32 * G::kRowBytes + koff[t]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
-            }
+        for (int i = 0; i < N - kQkAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
+#endif
     };
+    // The V^T operand of O^T for key step ks and head-dim block db: two transposed 8-byte reads.
+    auto v_operand = [&] __device__ (FA_LDS const char* vs, int ks, int db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][1]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 araw = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, araw);
+    };
+    // O^T += V_j^T P^T, with the V operands of the next key step read ahead.
     auto pv = [&] __device__ (FA_LDS const char* vs, const uint32_t (&pk)[16]) {
+        bf16x8 va[2][G::kDBlocks];
+#pragma unroll
+        for (int db = 0; db < G::kDBlocks; ++db) va[0][db] = v_operand(vs, 0, db);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int db = 0; db < G::kDBlocks; ++db) va[(ks + 1) & 1][db] = v_operand(vs, ks + 1, db);
+            }
             const u32x4 praw = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
             const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db) {
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][0]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (FA_LDS i16x4*)(vs + ks * 16 * G::kRowBytes + voff[db][1]));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                const u32x4 araw = {l2[0], l2[1], h2[0], h2[1]};
-                st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, araw), pb, st.o[db],
-                                                                    0, 0, 0);
+            for (int db = 0; db < G::kDBlocks; ++db)
+                st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][db], pb, st.o[db], 0, 0, 0);
+        }
+    };
+
+    f32x16 sc[2];       // score tile of the wave's current key tile
+    uint32_t pk[16];    // its bf16 weights, consumed by the next matrix phase
+
+    // PV of tile j fused with the scores of tile j+1, as one software-pipelined
+    // stream: the V operands of two key steps and the first K operands are in
+    // flight before the first MFMA, and the remaining K operands are fetched
+    // while the PV MFMAs run, so about 8 KB of LDS reads stay outstanding (LDS
+    // latency is a few hundred cycles; every MFMA consumes 1 KB of operands).
+    auto pv_qk = [&] __device__ (FA_LDS const char* vs, FA_LDS const char* ks) {
+        constexpr int NK = 2 * G::kDSteps;          // K operands (= QK MFMAs)
+        constexpr int NB = G::kDBlocks;             // PV MFMAs per key step
+        constexpr int K0 = 4;                       // K operands read before the first MFMA
+        constexpr int KPS = (NK - K0 + 3) / 4;      // K operands read per PV key step
+        bf16x8 va[4][NB];
+        bf16x8 ka[NK];
+#pragma unroll
+        for (int db = 0; db < NB; ++db) va[0][db] = v_operand(vs, 0, db);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) va[1][db] = v_operand(vs, 1, db);
+#pragma unroll
+        for (int i = 0; i < K0; ++i) ka[i] = *(FA_LDS const bf16x8*)(ks + (i & 1) * 32 * G::kRowBytes + koff[i >> 1]);
+#pragma unroll
+        for (int st4 = 0; st4 < 4; ++st4) {
+            const u32x4 praw = {pk[4 * st4], pk[4 * st4 + 1], pk[4 * st4 + 2], pk[4 * st4 + 3]};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
+#pragma unroll
+            for (int db = 0; db < NB; ++db)
+                st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st4][db], pb, st.o[db], 0, 0, 0);
+            if (st4 + 2 < 4) {
+#pragma unroll
+                for (int db = 0; db < NB; ++db) va[st4 + 2][db] = v_operand(vs, st4 + 2, db);
             }
-        }
-    };
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads have landed
-    __syncthreads();
-
-    // Two score buffers: even steps turn sa into probabilities while sb fills, odd
-    // steps the other way round (a static register renaming, no copies).
-    f32x16 sa[2], sb[2];
-#if FA_PIPELINE
-    if (n_w > 0) {
-        qk(kslot[0], sa);
-        if (n_w > 1) st.m = tile_max(sa) * c;
-    }
-#endif
-
-    // Tiles every wave of the workgroup treats as unmasked, with a successor:
-    // wave 0 has the fewest tiles, and its last one is left to the tail.
-    const int n_w0 = qt * kBM >= T ? 0 : (CAUSAL ? min(n_all, (qt * kBM + 31) / kBN + 1) : n_all);
-    const int n_steady = max(0, n_w0 - 1);
-
-    // Steady tile j (parity P): tile j+1's score MFMAs overlap tile j's
-    // exponentials; tile j+1's max is taken while tile j's PV MFMAs run.
-    auto steady = [&] __device__ (int j, auto parity, f32x16 (&sc)[2], f32x16 (&sn)[2], bool next_steady) {
-        constexpr int P = decltype(parity)::value;   // j % 2
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();   // K_{j+1}, V_j landed; every wave is done with K_j and V_{j-1}
-        if (j + 2 < n_kt) load_tile(kbh, (j + 2) * kBN, kslot[P]);
-        if (j + 1 < n_kt) load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
-        qk(kslot[P ^ 1], sn);
-        uint32_t pk[16];
-        const float mneg = -st.m;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const float x0 = n < 8 ? sc[0][2 * n] : sc[1][2 * n - 16];
-            const float x1 = n < 8 ? sc[0][2 * n + 1] : sc[1][2 * n - 15];
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, mneg));
-            st.l32 += p0;
-            st.l32 += p1;
-            pk[n] = pack_bf16x2(p0, p1);
+            for (int i = K0 + st4 * KPS; i < K0 + (st4 + 1) * KPS && i < NK; ++i)
+                ka[i] = *(FA_LDS const bf16x8*)(ks + (i & 1) * 32 * G::kRowBytes + koff[i >> 1]);
         }
-        pv(vslot[P], pk);
 #pragma unroll
-        for (int n = 0; n < 16; ++n)
-            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
-        if (next_steady) maybe_rescale<D>(st, tile_max(sn) * c);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[b][i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+            sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
+        // pin the order written above
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NB + K0, 0);
+        sgb_pv_step<NK, NB, K0, KPS, 0>();
+        sgb_pv_step<NK, NB, K0, KPS, 1>();
+        sgb_pv_step<NK, NB, K0, KPS, 2>();
+        sgb_pv_step<NK, NB, K0, KPS, 3>();
+        __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
     };
 
-    // Steady tile j without the in-wave pipeline: scores, max, weights, PV.
-    auto steady_np = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
+    // Matrix phase for tile j (parity P = j & 1): PV of tile j, then the scores
+    // of tile j+1 (K_{j+1} sits in slot P ^ 1, V_j in slot P).
+    auto matrix_phase = [&] __device__ (int j, auto parity) {
         constexpr int P = decltype(parity)::value;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();   // K_j, V_j landed; every wave is done with K_{j-1}, V_{j-1}
-        if (j + 1 < n_kt) {
-            load_tile(kbh, (j + 1) * kBN, kslot[P ^ 1]);
-            load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
-        }
-        qk(kslot[P], sc);
-        maybe_rescale<D>(st, tile_max(sc) * c);
-        uint32_t pk[16];
-        const float mneg = -st.m;
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const float x0 = n < 8 ? sc[0][2 * n] : sc[1][2 * n - 16];
-            const float x1 = n < 8 ? sc[0][2 * n + 1] : sc[1][2 * n - 15];
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c, mneg));
-            st.l32 += p0;
-            st.l32 += p1;
-            pk[n] = pack_bf16x2(p0, p1);
-            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
-        }
-        pv(vslot[P], pk);
-    };
-
-    // A wave's last tile (parity P): mask keys past its diagonal or past T.
-    auto last = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
-        constexpr int P = decltype(parity)::value;
-        const int key0 = j * kBN;
-        float x[32];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool vis = key < T && (!CAUSAL || key <= qrow);
-                x[kb * 16 + i] = vis ? sc[kb][i] * c : -INFINITY;
-            }
-        float mt = x[0];
-#pragma unroll
-        for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-        maybe_rescale<D>(st, fmaxf(st.m, xhalf_max(mt)));
-        const float mu = st.m == -INFINITY ? 0.0f : st.m;
-        uint32_t pk[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const float p0 = __builtin_amdgcn_exp2f(x[2 * n] - mu);
-            const float p1 = __builtin_amdgcn_exp2f(x[2 * n + 1] - mu);
-            st.l32 += p0;
-            st.l32 += p1;
-            pk[n] = pack_bf16x2(p0, p1);
-            st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
-        }
-        pv(vslot[P], pk);
-    };
-
-    // Tail tile j (parity P): per-wave steady / last / idle, plus the loads.
-    auto tail = [&] __device__ (int j, auto parity, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-        constexpr int P = decltype(parity)::value;
-        if (j + 1 < n_w) {
-            steady(j, parity, sc, sn, j + 2 < n_w);
+        // Issue priority for the matrix phase: otherwise the older waves' softmax
+        // work wins the SIMD's arbitration and starves the other group's MFMAs.
+        __builtin_amdgcn_s_setprio(FA_MATRIX_PRIO);
+        const bool do_pv = j >= 0 && j < n_w;
+        const bool do_qk = j + 1 < n_w;
+        if (FA_FUSED_PVQK && do_pv && do_qk) {
+            pv_qk(vslot[P], kslot[P ^ 1]);
         } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
-            if (j + 2 < n_kt) load_tile(kbh, (j + 2) * kBN, kslot[P]);
-            if (j + 1 < n_kt) load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
-            if (j + 1 == n_w) last(j, parity, sc);
+            if (do_pv) pv(vslot[P], pk);
+            if (do_qk) qk(kslot[P ^ 1], sc);
+        }
+        if (do_pv) {
+#pragma unroll
+            for (int n = 0; n < 16; ++n)
+                st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // Softmax phase for tile j: running max, weights, fp32 row sum.
+    auto softmax_phase = [&] __device__ (int j) {
+        if (j < 0 || j >= n_w) return;
+        if (j + 1 < n_w) {
+            if (!FA_SPECULATE) {
+                maybe_rescale<D>(st, tile_max(sc) * c);
+            }
+            // Weights against the current reference.  With speculation the tile
+            // max is only taken when some weight may exceed 2^8, detected by the
+            // lane's tile sum exceeding 2^8 (every weight is then <= 2^8 otherwise).
+            float p[32];
+            float ts;
+            auto weights = [&] __device__ () {
+                const float mneg = -st.m;
+#pragma unroll
+                for (int n = 0; n < 32; ++n)
+                    p[n] = __builtin_amdgcn_exp2f(__builtin_fmaf(n < 16 ? sc[0][n] : sc[1][n - 16], c, mneg));
+                float t8[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) t8[q] = (p[4 * q] + p[4 * q + 1]) + (p[4 * q + 2] + p[4 * q + 3]);
+                ts = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+            };
+            weights();
+            if (FA_SPECULATE && __any(!(ts <= 256.0f))) {
+                maybe_rescale<D>(st, tile_max(sc) * c);
+                weights();
+            }
+            st.l32 += ts;
+#pragma unroll
+            for (int n = 0; n < 16; ++n) pk[n] = pack_bf16x2(p[2 * n], p[2 * n + 1]);
+        } else {
+            // A wave's last tile: mask keys past its diagonal or past T.
+            const int key0 = j * kBN;
+            float x[32];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool vis = key < T && (!CAUSAL || key <= qrow);
+                    x[kb * 16 + i] = vis ? sc[kb][i] * c : -INFINITY;
+                }
+            float mt = x[0];
+#pragma unroll
+            for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
+            maybe_rescale<D>(st, fmaxf(st.m, xhalf_max(mt)));
+            const float mu = st.m == -INFINITY ? 0.0f : st.m;
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                const float p0 = __builtin_amdgcn_exp2f(x[2 * n] - mu);
+                const float p1 = __builtin_amdgcn_exp2f(x[2 * n + 1] - mu);
+                st.l32 += p0;
+                st.l32 += p1;
+                pk[n] = pack_bf16x2(p0, p1);
+            }
         }
     };
 
+    // Phase ph: the leading group runs step ph, the trailing group step ph - 1,
+    // where the steps are M(-1), S(0), M(0), S(1), M(1), ... (M = matrix phase,
+    // S = softmax phase).  Even phases 2 j first wait for the loads issued two
+    // phases earlier, then fetch K_{j+1} and V_j into the slots freed by M(j-2).
     using Even = std::integral_constant<int, 0>;
     using Odd = std::integral_constant<int, 1>;
-#if !FA_PIPELINE
-    // Non-pipelined order: K_j and V_j share a stage; tile j+1 loads during tile j.
-    auto tail_np = [&] __device__ (int j, auto parity, f32x16 (&sc)[2]) {
-        constexpr int P = decltype(parity)::value;
-        if (j + 1 < n_w) {
-            steady_np(j, parity, sc);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+    const int n_ph = 2 * n_kt + 2;
+    // Barrier + loads at the start of phase ph (identical in both groups' loops).
+    auto phase_start = [&] __device__ (int ph) {
+        if ((ph & 1) == 0) {
+            const int j = ph >> 1;
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loads of phase ph - 2 have landed
             __syncthreads();
-            if (j + 1 < n_kt) {
-                load_tile(kbh, (j + 1) * kBN, kslot[P ^ 1]);
-                load_tile(vbh, (j + 1) * kBN, vslot[P ^ 1]);
-            }
-            if (j + 1 == n_w) {
-                qk(kslot[P], sc);
-                last(j, parity, sc);
-            }
+            if (j + 1 < n_kt) load_tile(kbh, (j + 1) * kBN, kslot[(j + 1) & 1]);
+            if (j < n_kt) load_tile(vbh, j * kBN, vslot[j & 1]);
+        } else if (FA_ODD_BARRIER) {
+            __syncthreads();
         }
     };
-    int j = 0;
-    for (; j + 1 < n_steady; j += 2) {
-        steady_np(j, Even{}, sa);
-        steady_np(j + 1, Odd{}, sa);
+    // Each group runs its own straight-line loop; both loops pass the same
+    // sequence of barriers.  Four phases (two key tiles) per iteration keep the
+    // LDS slot of every access a compile-time constant.
+    if (grp == 0) {
+        for (int ph = 0; ph < n_ph; ph += 4) {
+            const int j = ph >> 1;
+            phase_start(ph);
+            matrix_phase(j - 1, Odd{});
+            if (ph + 1 >= n_ph) break;
+            phase_start(ph + 1);
+            softmax_phase(j);
+            if (ph + 2 >= n_ph) break;
+            phase_start(ph + 2);
+            matrix_phase(j, Even{});
+            if (ph + 3 >= n_ph) break;
+            phase_start(ph + 3);
+            softmax_phase(j + 1);
+        }
+    } else {
+        for (int ph = 0; ph < n_ph; ph += 4) {
+            const int j = ph >> 1;
+            phase_start(ph);
+            softmax_phase(j - 1);
+            if (ph + 1 >= n_ph) break;
+            phase_start(ph + 1);
+            matrix_phase(j - 1, Odd{});
+            if (ph + 2 >= n_ph) break;
+            phase_start(ph + 2);
+            softmax_phase(j);
+            if (ph + 3 >= n_ph) break;
+            phase_start(ph + 3);
+            matrix_phase(j, Even{});
+        }
     }
-    for (; j < n_kt; j += 2) {
-        if (j < n_steady) steady_np(j, Even{}, sa);
-        else tail_np(j, Even{}, sa);
-        if (j + 1 < n_kt) tail_np(j + 1, Odd{}, sa);
-    }
-#else
-    int j = 0;
-    for (; j + 1 < n_steady; j += 2) {
-        steady(j, Even{}, sa, sb, true);
-        steady(j + 1, Odd{}, sb, sa, true);
-    }
-    // Tiles n_steady_even .. n_kt-1: the odd leftover steady tile and the masked ends.
-    for (; j < n_kt; j += 2) {
-        if (j < n_steady) steady(j, Even{}, sa, sb, true);
-        else tail(j, Even{}, sa, sb);
-        if (j + 1 < n_kt) tail(j + 1, Odd{}, sb, sa);
-    }
-#endif
 
     // Epilogue: O = o / l (bf16, round to nearest even), lse = ln2 * (m + log2 l).
     const float l32 = xhalf_sum(st.l32);
@@ -491,7 +558,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU, FA_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                    int T, int n_qt, int total, float c_in /* scale * log2(e) */) {
