@@ -21,11 +21,12 @@
 //     for P) and its accumulator again keeps one query row per lane, so a row's
 //     rescale factor is lane-local.
 //   * Ping-pong between the two waves of a SIMD.  Waves 0-3 run one phase ahead
-//     of waves 4-7, and a workgroup barrier separates phases, so in every phase
-//     one wave of each SIMD runs a matrix phase (PV of tile j and S^T of tile
-//     j+1: 32 MFMAs) while the other runs a softmax phase (max, exponentials,
-//     row sums of tile j+1: VALU work).  The two kinds of work then co-issue on
-//     the SIMD instead of competing for the same unit.  This is the
+//     of waves 4-7, and a workgroup barrier at every key tile (every second
+//     phase) keeps them there, so one wave of each SIMD runs a matrix phase (PV
+//     of tile j and S^T of tile j+1: 32 MFMAs, at raised wave priority) while
+//     the other runs a softmax phase (max, exponentials, row sums of tile j+1:
+//     VALU work).  The two kinds of work then co-issue on the SIMD instead of
+//     competing for the same unit.  This is the
 //     producer/consumer overlap of softmax with the matrix products described
 //     for FlashAttention-3 on "FlashAttention and Fused Kernels: Attention
 //     Without the n x n Matrix" ("Four generations"), done here with wave groups
@@ -44,7 +45,10 @@
 //     exceeds the running reference by more than 2^8 (in exp2 units), the
 //     conditional rescale described for FlashAttention-4 on the same page.
 //     Weights exp2(x - m) then stay at most 256, and the result is unchanged up
-//     to rounding.  Two row sums are kept: the fp32 sum of the weights (for the
+//     to rounding.  The weights are first computed against the current
+//     reference; only when some lane's tile sum exceeds 256 (so that some weight
+//     may) is the tile max taken and the weights recomputed, which gives the
+//     same bits as always taking the max.  Two row sums are kept: the fp32 sum of the weights (for the
 //     log-sum-exp) and the sum of their bf16 roundings, which are the weights
 //     the PV product actually used (for O = o / l).
 //   * Causal: key tiles past a wave's last query are skipped; only a wave's

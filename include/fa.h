@@ -37,7 +37,8 @@ typedef enum {
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte   */
-    FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid */
+    FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid,
+                             or one head (T*d*2 bytes plus 2 row tiles) >= 4 GiB */
     FA_ERR_HIP = 7,       /* the kernel launch failed; see fa_hip_error_string()  */
     FA_ERR_ARG = 8        /* causal not 0/1, or an output overlaps an input       */
 } fa_status;
