@@ -175,7 +175,10 @@ __device__ __forceinline__ void sgb_pv_step() {
 template <int D>
 struct WaveState {
     f32x16 o[Geo<D>::kDBlocks];   // O^T accumulator: lane holds d-rows of its query
-    float m = -INFINITY;          // running reference max (exp2 units)
+    // Running reference max (exp2 units).  It starts at the most negative
+    // finite float rather than -inf, so that the first tile's weights are +inf
+    // (never NaN, also for masked -inf scores) and take the max.
+    float m = -3.402823466e38f;
     float l32 = 0.0f;             // sum of fp32 weights
     float l16 = 0.0f;             // sum of bf16-rounded weights
 };
@@ -284,7 +287,10 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             qf[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
-    const float c = fabsf(c_in);
+    // A zero scale runs as 1e-30: every product s * c then rounds away against
+    // the reference in exp2 (all weights are 1, as for zero), and masked scores
+    // (-inf) still give -inf instead of -inf * 0 = NaN.
+    const float c = fmaxf(fabsf(c_in), 1e-30f);
 
     WaveState<D> st;
 #pragma unroll
@@ -426,62 +432,49 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         }
         __builtin_amdgcn_s_setprio(0);
     };
-    // Softmax phase for tile j: running max, weights, fp32 row sum.
+    // Softmax phase for tile j: running max, weights, fp32 row sum.  Only a
+    // wave's last tile can cross its diagonal or the end of the sequence; there
+    // the hidden scores are set to -inf in place, so that every tile then takes
+    // the same path (a single code path keeps the O accumulator in place).
     auto softmax_phase = [&] __device__ (int j) {
         if (j < 0 || j >= n_w) return;
-        if (j + 1 < n_w) {
-            if (!FA_SPECULATE) {
-                maybe_rescale<D>(st, tile_max(sc) * c);
-            }
-            // Weights against the current reference.  With speculation the tile
-            // max is only taken when some weight may exceed 2^8, detected by the
-            // lane's tile sum exceeding 2^8 (every weight is then <= 2^8 otherwise).
-            float p[32];
-            float ts;
-            auto weights = [&] __device__ () {
-                const float mneg = -st.m;
-#pragma unroll
-                for (int n = 0; n < 32; ++n)
-                    p[n] = __builtin_amdgcn_exp2f(__builtin_fmaf(n < 16 ? sc[0][n] : sc[1][n - 16], c, mneg));
-                float t8[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) t8[q] = (p[4 * q] + p[4 * q + 1]) + (p[4 * q + 2] + p[4 * q + 3]);
-                ts = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
-            };
-            weights();
-            if (FA_SPECULATE && __any(!(ts <= 256.0f))) {
-                maybe_rescale<D>(st, tile_max(sc) * c);
-                weights();
-            }
-            st.l32 += ts;
-#pragma unroll
-            for (int n = 0; n < 16; ++n) pk[n] = pack_bf16x2(p[2 * n], p[2 * n + 1]);
-        } else {
-            // A wave's last tile: mask keys past its diagonal or past T.
+        if (j == n_w - 1) {
             const int key0 = j * kBN;
-            float x[32];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
                     const bool vis = key < T && (!CAUSAL || key <= qrow);
-                    x[kb * 16 + i] = vis ? sc[kb][i] * c : -INFINITY;
+                    sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
                 }
-            float mt = x[0];
-#pragma unroll
-            for (int i = 1; i < 32; ++i) mt = fmaxf(mt, x[i]);
-            maybe_rescale<D>(st, fmaxf(st.m, xhalf_max(mt)));
-            const float mu = st.m == -INFINITY ? 0.0f : st.m;
-#pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                const float p0 = __builtin_amdgcn_exp2f(x[2 * n] - mu);
-                const float p1 = __builtin_amdgcn_exp2f(x[2 * n + 1] - mu);
-                st.l32 += p0;
-                st.l32 += p1;
-                pk[n] = pack_bf16x2(p0, p1);
-            }
         }
+        if (!FA_SPECULATE) maybe_rescale<D>(st, tile_max(sc) * c);
+        // Weights against the current reference.  With speculation the tile max
+        // is only taken when some weight may exceed 2^8, detected by the lane's
+        // tile sum exceeding 2^8 (every weight is <= 2^8 otherwise).  Before the
+        // first rescale the reference is -FLT_MAX and the visible weights are
+        // inf, which also takes the max.
+        float p[32];
+        float ts;
+        auto weights = [&] __device__ () {
+            const float mneg = -st.m;
+#pragma unroll
+            for (int n = 0; n < 32; ++n)
+                p[n] = __builtin_amdgcn_exp2f(__builtin_fmaf(n < 16 ? sc[0][n] : sc[1][n - 16], c, mneg));
+            float t8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) t8[q] = (p[4 * q] + p[4 * q + 1]) + (p[4 * q + 2] + p[4 * q + 3]);
+            ts = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+        };
+        weights();
+        if (FA_SPECULATE && __any(!(ts <= 256.0f))) {
+            maybe_rescale<D>(st, tile_max(sc) * c);
+            weights();
+        }
+        st.l32 += ts;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) pk[n] = pack_bf16x2(p[2 * n], p[2 * n + 1]);
     };
 
     // Phase ph: the leading group runs step ph, the trailing group step ph - 1,
