@@ -78,10 +78,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256;        // query rows per workgroup (8 waves x 32 rows)
 constexpr int kBN = 64;         // keys per K/V tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -101,8 +98,13 @@ constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor w
 #endif
 
 
-template <int D>
+// Tile geometry for head size D and NG wave groups per workgroup (4 waves of
+// 32 query rows each per group).
+template <int D, int NG>
 struct Geo {
+    static constexpr int kWaves = 4 * NG;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBM = 32 * kWaves;          // query rows per workgroup
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;            // 16-byte chunks per row
     static constexpr int kTileBytes = kBN * kRowBytes;
@@ -174,7 +176,7 @@ __device__ __forceinline__ void sgb_pv_step() {
 
 template <int D>
 struct WaveState {
-    f32x16 o[Geo<D>::kDBlocks];   // O^T accumulator: lane holds d-rows of its query
+    f32x16 o[Geo<D, 1>::kDBlocks];   // O^T accumulator: lane holds d-rows of its query
     // Running reference max (exp2 units).  It starts at the most negative
     // finite float rather than -inf, so that the first tile's weights are +inf
     // (never NaN, also for masked -inf scores) and take the max.
@@ -193,26 +195,27 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float m_new) {
         st.l32 *= r;
         st.l16 *= r;
 #pragma unroll
-        for (int b = 0; b < Geo<D>::kDBlocks; ++b)
+        for (int b = 0; b < Geo<D, 1>::kDBlocks; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) st.o[b][i] *= r;
     }
 }
 
 
-// One workgroup's work; `lds` is the workgroup's Geo<D>::kLdsBytes of LDS.
-template <int D, bool CAUSAL>
+// One workgroup's work; `lds` is the workgroup's Geo<D, NG>::kLdsBytes of LDS.
+template <int D, bool CAUSAL, int NG>
 __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                              float* __restrict__ LSE, int T, int n_qt, int total, float c_in,
                                              FA_LDS char* const lds) {
-    using G = Geo<D>;
+    using G = Geo<D, NG>;
+    constexpr int kBM = G::kBM;
     FA_LDS char* const kslot[2] = {lds, lds + G::kTileBytes};
     FA_LDS char* const vslot[2] = {lds + 2 * G::kTileBytes, lds + 3 * G::kTileBytes};
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave >> 2;   // 0: leading wave group, 1: one phase behind
+    const int grp = NG == 2 ? wave >> 2 : 0;   // 0: leading wave group, 1: one phase behind
     const int col = lane & 31;   // this lane's query row within the wave
     const int half = lane >> 5;
 
@@ -554,13 +557,15 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Two waves per SIMD: NG = 2 is one 8-wave workgroup per CU whose wave groups
+// alternate phases; NG = 1 is two independent 4-wave workgroups per CU.
+template <int D, bool CAUSAL, int NG>
+__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                    int T, int n_qt, int total, float c_in /* scale * log2(e) */) {
-    __shared__ __attribute__((aligned(1024))) char smem[Geo<D>::kLdsBytes];
-    fa_fwd_block<D, CAUSAL>(Q, K, V, O, LSE, T, n_qt, total, c_in, (FA_LDS char*)smem);
+    __shared__ __attribute__((aligned(1024))) char smem[Geo<D, NG>::kLdsBytes];
+    fa_fwd_block<D, CAUSAL, NG>(Q, K, V, O, LSE, T, n_qt, total, c_in, (FA_LDS char*)smem);
 }
 
 thread_local char g_hip_error[256] = "";
@@ -570,10 +575,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NG>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int T, int n_qt, int total,
                   float c, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, NG>), dim3(total), dim3(Geo<D, NG>::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, T, n_qt, total, c);
     return hipGetLastError();
@@ -592,6 +597,16 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if ((addr(q) | addr(k) | addr(v) | addr(o)) & 15u) return FA_ERR_ALIGN;
     if (addr(lse) & 3u) return FA_ERR_ALIGN;
 
+    // Workgroup shape: the phase-alternating 8-wave workgroup pays off when
+    // d = 128 and each query tile walks many key tiles (T >= 8192 causal, or
+    // T >= 4096 without the mask); otherwise two independent 4-wave workgroups
+    // per CU are faster.  Both shapes give bit-identical results.
+#ifndef FA_FORCE_GROUPS
+#define FA_FORCE_GROUPS 0
+#endif
+    const int ng = FA_FORCE_GROUPS ? FA_FORCE_GROUPS : (d == 128 && T * (causal ? 1 : 2) >= 8192 ? 2 : 1);
+    const int64_t bm = 128 * ng;
+
     // Sizes: every byte count must fit int64; in-kernel row indices are 32-bit.
     const int64_t kMax = INT64_MAX;
     if (B > kMax / H) return FA_ERR_OVERFLOW;
@@ -599,10 +614,10 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if (BH > kMax / T) return FA_ERR_OVERFLOW;
     const int64_t rows = BH * T;
     if (rows > kMax / (2 * d)) return FA_ERR_OVERFLOW;
-    if (T > INT32_MAX - 2 * kBM) return FA_ERR_OVERFLOW;
+    if (T > INT32_MAX - 2 * bm) return FA_ERR_OVERFLOW;
     // Buffer descriptors address one head: (T + 2 query tiles) rows must fit in 32-bit byte offsets.
-    if ((T + 2 * kBM) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
-    const int64_t n_qt = (T + kBM - 1) / kBM;
+    if ((T + 2 * bm) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
+    const int64_t n_qt = (T + bm - 1) / bm;
     if (BH > INT32_MAX / n_qt) return FA_ERR_OVERFLOW;
     const int total = static_cast<int>(BH * n_qt);
 
@@ -615,14 +630,23 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if (overlaps(o, tensor_bytes, lse, lse_bytes)) return FA_ERR_ARG;
 
     const float c = static_cast<float>(static_cast<double>(scale) * kLog2e);
-    hipError_t err;
     const int Ti = static_cast<int>(T), nq = static_cast<int>(n_qt);
-    if (d == 128)
-        err = causal ? launch<128, true>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                     : launch<128, false>(q, k, v, o, lse, Ti, nq, total, c, stream);
-    else
-        err = causal ? launch<64, true>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                     : launch<64, false>(q, k, v, o, lse, Ti, nq, total, c, stream);
+    hipError_t err;
+    if (d == 128) {
+        if (ng == 2)
+            err = causal ? launch<128, true, 2>(q, k, v, o, lse, Ti, nq, total, c, stream)
+                         : launch<128, false, 2>(q, k, v, o, lse, Ti, nq, total, c, stream);
+        else
+            err = causal ? launch<128, true, 1>(q, k, v, o, lse, Ti, nq, total, c, stream)
+                         : launch<128, false, 1>(q, k, v, o, lse, Ti, nq, total, c, stream);
+    } else {
+        if (ng == 2)
+            err = causal ? launch<64, true, 2>(q, k, v, o, lse, Ti, nq, total, c, stream)
+                         : launch<64, false, 2>(q, k, v, o, lse, Ti, nq, total, c, stream);
+        else
+            err = causal ? launch<64, true, 1>(q, k, v, o, lse, Ti, nq, total, c, stream)
+                         : launch<64, false, 1>(q, k, v, o, lse, Ti, nq, total, c, stream);
+    }
     if (err != hipSuccess) {
         std::snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(err), hipGetErrorString(err));
         return FA_ERR_HIP;

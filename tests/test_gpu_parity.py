@@ -147,7 +147,7 @@ def test_workload_c5_sampled_rows_spiky(fa):
 # ---------------------------------------------------------------------------
 
 EDGE = [(1, 1, 1), (1, 1, 3), (1, 1, 4), (2, 1, 63), (1, 2, 64), (1, 1, 65), (1, 3, 127), (2, 2, 128),
-        (1, 1, 129), (1, 2, 200), (1, 1, 1000), (1, 1, 4097)]
+        (1, 1, 129), (1, 2, 200), (1, 1, 1000), (1, 1, 4097), (1, 1, 8200)]
 
 
 @pytest.mark.parametrize("d", [64, 128])
