@@ -224,8 +224,18 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     const int xcd = id % kXcds, xslot = id / kXcds;
     const int q8 = total / kXcds, r8 = total % kXcds;
     const int w = xcd < r8 ? xcd * (q8 + 1) + xslot : r8 * (q8 + 1) + (xcd - r8) * q8 + xslot;
-    const int bh = w / n_qt;
-    const int qt = CAUSAL ? n_qt - 1 - (w % n_qt) : (w % n_qt);
+    int bh = w / n_qt;
+    int qt = CAUSAL ? n_qt - 1 - (w % n_qt) : (w % n_qt);
+    // Causal work with few workgroups per CU (at most 8 rounds of the 256 CUs)
+    // is tail-bound: when every XCD owns whole heads, its heads are walked
+    // query-tile-major, so the heaviest tiles of all of them go first.  Longer
+    // grids keep the head-major order, which keeps one head's K/V in L2.
+    constexpr int kRoundSlots = 256 * (NG == 2 ? 1 : 2);   // CUs x workgroups per CU
+    if (CAUSAL && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
+        const int hx = q8 / n_qt;                 // heads per XCD
+        bh = xcd * hx + xslot % hx;
+        qt = n_qt - 1 - xslot / hx;
+    }
 
     const size_t base = (size_t)bh * (size_t)T * D;
     const uint16_t* __restrict__ kbh = K + base;
