@@ -366,8 +366,13 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             const u32x4 praw = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
             const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db)
+            for (int db = 0; db < G::kDBlocks; ++db) {
                 st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][db], pb, st.o[db], 0, 0, 0);
+                // The row sum of the bf16 weights rides in the MFMA shadow, in key order.
+#pragma unroll
+                for (int n = 4 * ks + db * 4 / G::kDBlocks; n < 4 * ks + (db + 1) * 4 / G::kDBlocks; ++n)
+                    st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
+            }
         }
     };
 
@@ -437,11 +442,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         } else {
             if (do_pv) pv(vslot[P], pk);
             if (do_qk) qk(kslot[P ^ 1], sc);
-        }
-        if (do_pv) {
-#pragma unroll
-            for (int n = 0; n < 16; ++n)
-                st.l16 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n]), ones, st.l16, false);
         }
         __builtin_amdgcn_s_setprio(0);
     };
