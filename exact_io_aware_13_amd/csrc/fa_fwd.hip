@@ -87,14 +87,8 @@ constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor w
 #ifndef FA_MATRIX_PRIO
 #define FA_MATRIX_PRIO 1
 #endif
-#ifndef FA_ODD_BARRIER
-#define FA_ODD_BARRIER 0
-#endif
 #ifndef FA_SPECULATE
 #define FA_SPECULATE 1
-#endif
-#ifndef FA_FUSED_PVQK
-#define FA_FUSED_PVQK 0
 #endif
 
 
@@ -163,16 +157,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Scheduling groups for PV key step S of the fused PV + QK stream: its NB
-// MFMAs, then the LDS reads issued after them (V two steps ahead, a share of K).
-template <int NK, int NB, int K0, int KPS, int S>
-__device__ __forceinline__ void sgb_pv_step() {
-    constexpr int lo = K0 + S * KPS < NK ? K0 + S * KPS : NK;
-    constexpr int hi = K0 + (S + 1) * KPS < NK ? K0 + (S + 1) * KPS : NK;
-    constexpr int reads = (S + 2 < 4 ? 2 * NB : 0) + (hi - lo);
-    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-    if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
-}
 
 template <int D>
 struct WaveState {
@@ -332,7 +316,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 #pragma unroll
         for (int i = 0; i < N; ++i)
             s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[i >> 1], s[i & 1], 0, 0, 0);
-#ifndef FA_NO_QK_SGB
         __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
 #pragma unroll
         for (int i = 0; i < N - kQkAhead; ++i) {
@@ -340,7 +323,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
-#endif
     };
     // The V^T operand of O^T for key step ks and head-dim block db: two transposed 8-byte reads.
     auto v_operand = [&] __device__ (FA_LDS const char* vs, int ks, int db) {
@@ -379,54 +361,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     f32x16 sc[2];       // score tile of the wave's current key tile
     uint32_t pk[16];    // its bf16 weights, consumed by the next matrix phase
 
-    // PV of tile j fused with the scores of tile j+1, as one software-pipelined
-    // stream: the V operands of two key steps and the first K operands are in
-    // flight before the first MFMA, and the remaining K operands are fetched
-    // while the PV MFMAs run, so about 8 KB of LDS reads stay outstanding (LDS
-    // latency is a few hundred cycles; every MFMA consumes 1 KB of operands).
-    auto pv_qk = [&] __device__ (FA_LDS const char* vs, FA_LDS const char* ks) {
-        constexpr int NK = 2 * G::kDSteps;          // K operands (= QK MFMAs)
-        constexpr int NB = G::kDBlocks;             // PV MFMAs per key step
-        constexpr int K0 = 4;                       // K operands read before the first MFMA
-        constexpr int KPS = (NK - K0 + 3) / 4;      // K operands read per PV key step
-        bf16x8 va[4][NB];
-        bf16x8 ka[NK];
-#pragma unroll
-        for (int db = 0; db < NB; ++db) va[0][db] = v_operand(vs, 0, db);
-#pragma unroll
-        for (int db = 0; db < NB; ++db) va[1][db] = v_operand(vs, 1, db);
-#pragma unroll
-        for (int i = 0; i < K0; ++i) ka[i] = *(FA_LDS const bf16x8*)(ks + (i & 1) * 32 * G::kRowBytes + koff[i >> 1]);
-#pragma unroll
-        for (int st4 = 0; st4 < 4; ++st4) {
-            const u32x4 praw = {pk[4 * st4], pk[4 * st4 + 1], pk[4 * st4 + 2], pk[4 * st4 + 3]};
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, praw);
-#pragma unroll
-            for (int db = 0; db < NB; ++db)
-                st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st4][db], pb, st.o[db], 0, 0, 0);
-            if (st4 + 2 < 4) {
-#pragma unroll
-                for (int db = 0; db < NB; ++db) va[st4 + 2][db] = v_operand(vs, st4 + 2, db);
-            }
-#pragma unroll
-            for (int i = K0 + st4 * KPS; i < K0 + (st4 + 1) * KPS && i < NK; ++i)
-                ka[i] = *(FA_LDS const bf16x8*)(ks + (i & 1) * 32 * G::kRowBytes + koff[i >> 1]);
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc[b][i] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-            sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], sc[i & 1], 0, 0, 0);
-        // pin the order written above
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NB + K0, 0);
-        sgb_pv_step<NK, NB, K0, KPS, 0>();
-        sgb_pv_step<NK, NB, K0, KPS, 1>();
-        sgb_pv_step<NK, NB, K0, KPS, 2>();
-        sgb_pv_step<NK, NB, K0, KPS, 3>();
-        __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
-    };
 
     // Matrix phase for tile j (parity P = j & 1): PV of tile j, then the scores
     // of tile j+1 (K_{j+1} sits in slot P ^ 1, V_j in slot P).
@@ -437,12 +371,8 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         __builtin_amdgcn_s_setprio(FA_MATRIX_PRIO);
         const bool do_pv = j >= 0 && j < n_w;
         const bool do_qk = j + 1 < n_w;
-        if (FA_FUSED_PVQK && do_pv && do_qk) {
-            pv_qk(vslot[P], kslot[P ^ 1]);
-        } else {
-            if (do_pv) pv(vslot[P], pk);
-            if (do_qk) qk(kslot[P ^ 1], sc);
-        }
+        if (do_pv) pv(vslot[P], pk);
+        if (do_qk) qk(kslot[P ^ 1], sc);
         __builtin_amdgcn_s_setprio(0);
     };
     // Softmax phase for tile j: running max, weights, fp32 row sum.  Only a
@@ -505,8 +435,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             __syncthreads();
             if (j + 1 < n_kt) load_tile(kbh, (j + 1) * kBN, kslot[(j + 1) & 1]);
             if (j < n_kt) load_tile(vbh, j * kBN, vslot[j & 1]);
-        } else if (FA_ODD_BARRIER) {
-            __syncthreads();
         }
     };
     // Each group runs its own straight-line loop; both loops pass the same
