@@ -56,6 +56,12 @@ def _load():
                                             ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64,
                                             dp, dp]
         lib.fa_ref_fwd_rows_f64.restype = ctypes.c_int
+        lib.fa_ref_attn_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_double]
+        lib.fa_ref_attn_f64.restype = ctypes.c_int
+        lib.fa_ref_attn_rows_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64, dp, dp]
+        lib.fa_ref_attn_rows_f64.restype = ctypes.c_int
         lib.fa_ref_num_threads.argtypes = []
         lib.fa_ref_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -80,48 +86,58 @@ def _as_f64(x) -> np.ndarray:
 
 
 def _check4(q, k, v):
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError(f"q, k, v must share one (B, H, T, d) shape; got {q.shape}, {k.shape}, {v.shape}")
+    """q: (B, Hq, Tq, d); k, v: (B, Hkv, Tk, d) with Hq a multiple of Hkv."""
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError(f"q must be (B, Hq, Tq, d) and k, v one (B, Hkv, Tk, d) shape; got "
+                         f"{q.shape}, {k.shape}, {v.shape}")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3] or q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"incompatible q {q.shape} and k/v {k.shape}")
 
 
 def attention_f64(q, k, v, causal: bool, scale: float):
     """Exact attention forward over every row.
 
-    ``q, k, v``: (B, H, T, d) arrays, either float64/float32 values or uint16
-    bf16 bit patterns (widened exactly).  Returns ``(o, lse)`` as float64 with
-    shapes (B, H, T, d) and (B, H, T); ``lse`` is in natural-log units.
+    ``q``: (B, Hq, Tq, d); ``k, v``: (B, Hkv, Tk, d), Hq a multiple of Hkv
+    (query head h reads key/value head h // (Hq // Hkv)); either float64/float32
+    values or uint16 bf16 bit patterns (widened exactly).  With ``causal`` the
+    queries are the last Tq positions: query i sees keys j <= i + Tk - Tq.
+    Returns ``(o, lse)`` as float64 with shapes (B, Hq, Tq, d) and (B, Hq, Tq);
+    ``lse`` is in natural-log units.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     _check4(q, k, v)
-    B, H, T, d = q.shape
-    o = np.empty((B, H, T, d), dtype=np.float64)
-    lse = np.empty((B, H, T), dtype=np.float64)
-    rc = _load().fa_ref_fwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
-                                B, H, T, d, int(bool(causal)), float(scale))
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    o = np.empty((B, Hq, Tq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, Tq), dtype=np.float64)
+    rc = _load().fa_ref_attn_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                 B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale))
     if rc != 0:
-        raise RuntimeError(f"fa_ref_fwd_f64 failed with code {rc}")
+        raise RuntimeError(f"fa_ref_attn_f64 failed with code {rc}")
     return o, lse
 
 
 def attention_rows_f64(q, k, v, causal: bool, scale: float, rows):
     """Exact attention forward for selected rows only.
 
-    ``rows`` holds flat row indices ``(b*H + h)*T + i``.  Returns
-    ``(o_rows, lse_rows)`` with shapes (n, d) and (n,).
+    Shapes and rules as ``attention_f64``; ``rows`` holds flat row indices
+    ``(b*Hq + h)*Tq + i``.  Returns ``(o_rows, lse_rows)`` with shapes (n, d)
+    and (n,).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     _check4(q, k, v)
-    B, H, T, d = q.shape
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = _load().fa_ref_fwd_rows_f64(_dptr(q), _dptr(k), _dptr(v), B, H, T, d,
-                                     int(bool(causal)), float(scale),
-                                     rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
-                                     _dptr(o), _dptr(lse))
+    rc = _load().fa_ref_attn_rows_f64(_dptr(q), _dptr(k), _dptr(v), B, Hq, Hkv, Tq, Tk, d,
+                                      int(bool(causal)), float(scale),
+                                      rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                      _dptr(o), _dptr(lse))
     if rc != 0:
-        raise RuntimeError(f"fa_ref_fwd_rows_f64 failed with code {rc}")
+        raise RuntimeError(f"fa_ref_attn_rows_f64 failed with code {rc}")
     return o, lse
 
 

@@ -70,27 +70,54 @@ static void attend_one_row(const double* qi, const double* kh, const double* vh,
     *lse_out = m + log(l);
 }
 
-static int sizes_ok(int64_t B, int64_t H, int64_t T, int64_t d)
+/*
+ * The general problem: Hq query heads over Hkv key/value heads (query head h
+ * reads key/value head h / (Hq / Hkv): consecutive query heads share one,
+ * the grouping of "FlashAttention and Fused Kernels: Attention Without the
+ * n x n Matrix", Step 4, for Llama 3.1 8B), Tq query rows over Tk keys.  With
+ * causal, the query rows are the last Tq positions of the Tk-long sequence:
+ * query i sees keys j <= i + (Tk - Tq) ("Flash Attention, tiled", section
+ * "Ordinary causal attention", for Tq = Tk; a decode row, Tq = 1, sees every
+ * cached key).  Causal needs Tq <= Tk so that every row sees a key.
+ */
+static int general_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal)
 {
-    return B >= 1 && H >= 1 && T >= 1 && d >= 1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1 || d < 1) return 0;
+    if (Hq % Hkv != 0) return 0;
+    if (causal && Tq > Tk) return 0;
+    return 1;
 }
 
-int fa_ref_fwd_rows_f64(const double* q, const double* k, const double* v,
-                        int64_t B, int64_t H, int64_t T, int64_t d,
-                        int causal, double scale,
-                        const int64_t* rows, int64_t n_rows,
-                        double* o_rows, double* lse_rows)
+/* Key/value head (b * Hkv + h / group) of flat query row `flat`. */
+static int64_t kv_head_of(int64_t flat, int64_t Hq, int64_t Hkv, int64_t Tq)
+{
+    const int64_t bh = flat / Tq;
+    const int64_t b = bh / Hq, h = bh % Hq;
+    return b * Hkv + h / (Hq / Hkv);
+}
+
+static int64_t visible_of(int64_t flat, int64_t Tq, int64_t Tk, int causal)
+{
+    const int64_t i = flat % Tq;
+    return causal ? i + (Tk - Tq) + 1 : Tk;
+}
+
+int fa_ref_attn_rows_f64(const double* q, const double* k, const double* v,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                         int causal, double scale,
+                         const int64_t* rows, int64_t n_rows,
+                         double* o_rows, double* lse_rows)
 {
     if (!q || !k || !v || !rows || !o_rows || !lse_rows) return -1;
-    if (!sizes_ok(B, H, T, d) || n_rows < 0) return -1;
-    const int64_t n_total = B * H * T;
+    if (!general_ok(B, Hq, Hkv, Tq, Tk, d, causal) || n_rows < 0) return -1;
+    const int64_t n_total = B * Hq * Tq;
     for (int64_t r = 0; r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= n_total) return -1;
 
     int failed = 0;
 #pragma omp parallel
     {
-        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* s = (double*)malloc((size_t)Tk * sizeof(double));
         if (!s) {
 #pragma omp atomic write
             failed = 1;
@@ -99,12 +126,9 @@ int fa_ref_fwd_rows_f64(const double* q, const double* k, const double* v,
         for (int64_t r = 0; r < n_rows; ++r) {
             if (!s) continue;
             const int64_t flat = rows[r];
-            const int64_t bh = flat / T;     /* b*H + h */
-            const int64_t i = flat % T;
-            const double* kh = k + bh * T * d;
-            const double* vh = v + bh * T * d;
-            const int64_t n_vis = causal ? i + 1 : T;
-            attend_one_row(q + flat * d, kh, vh, n_vis, d, scale, s,
+            const int64_t kvh = kv_head_of(flat, Hq, Hkv, Tq);
+            attend_one_row(q + flat * d, k + kvh * Tk * d, v + kvh * Tk * d,
+                           visible_of(flat, Tq, Tk, causal), d, scale, s,
                            o_rows + r * d, lse_rows + r);
         }
         free(s);
@@ -112,19 +136,19 @@ int fa_ref_fwd_rows_f64(const double* q, const double* k, const double* v,
     return failed ? -2 : 0;
 }
 
-int fa_ref_fwd_f64(const double* q, const double* k, const double* v,
-                   double* o, double* lse,
-                   int64_t B, int64_t H, int64_t T, int64_t d,
-                   int causal, double scale)
+int fa_ref_attn_f64(const double* q, const double* k, const double* v,
+                    double* o, double* lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                    int causal, double scale)
 {
     if (!q || !k || !v || !o || !lse) return -1;
-    if (!sizes_ok(B, H, T, d)) return -1;
-    const int64_t n_total = B * H * T;
+    if (!general_ok(B, Hq, Hkv, Tq, Tk, d, causal)) return -1;
+    const int64_t n_total = B * Hq * Tq;
 
     int failed = 0;
 #pragma omp parallel
     {
-        double* s = (double*)malloc((size_t)T * sizeof(double));
+        double* s = (double*)malloc((size_t)Tk * sizeof(double));
         if (!s) {
 #pragma omp atomic write
             failed = 1;
@@ -132,15 +156,31 @@ int fa_ref_fwd_f64(const double* q, const double* k, const double* v,
 #pragma omp for schedule(dynamic, 16)
         for (int64_t flat = 0; flat < n_total; ++flat) {
             if (!s) continue;
-            const int64_t bh = flat / T;
-            const int64_t i = flat % T;
-            const int64_t n_vis = causal ? i + 1 : T;
-            attend_one_row(q + flat * d, k + bh * T * d, v + bh * T * d,
-                           n_vis, d, scale, s, o + flat * d, lse + flat);
+            const int64_t kvh = kv_head_of(flat, Hq, Hkv, Tq);
+            attend_one_row(q + flat * d, k + kvh * Tk * d, v + kvh * Tk * d,
+                           visible_of(flat, Tq, Tk, causal), d, scale, s, o + flat * d, lse + flat);
         }
         free(s);
     }
     return failed ? -2 : 0;
+}
+
+/* The square problem with one key/value head per query head. */
+int fa_ref_fwd_rows_f64(const double* q, const double* k, const double* v,
+                        int64_t B, int64_t H, int64_t T, int64_t d,
+                        int causal, double scale,
+                        const int64_t* rows, int64_t n_rows,
+                        double* o_rows, double* lse_rows)
+{
+    return fa_ref_attn_rows_f64(q, k, v, B, H, H, T, T, d, causal, scale, rows, n_rows, o_rows, lse_rows);
+}
+
+int fa_ref_fwd_f64(const double* q, const double* k, const double* v,
+                   double* o, double* lse,
+                   int64_t B, int64_t H, int64_t T, int64_t d,
+                   int causal, double scale)
+{
+    return fa_ref_attn_f64(q, k, v, o, lse, B, H, H, T, T, d, causal, scale);
 }
 
 int fa_ref_num_threads(void)

@@ -56,6 +56,22 @@ int fa_ref_fwd_rows_f64(const double* q, const double* k, const double* v,
                         const int64_t* rows, int64_t n_rows,
                         double* o_rows, double* lse_rows);
 
+/* The general problem: q, o are [B][Hq][Tq][d], k, v are [B][Hkv][Tk][d];
+ * query head h reads key/value head h / (Hq / Hkv); with causal, query i sees
+ * keys j <= i + (Tk - Tq) (the queries are the last Tq positions).  Needs
+ * Hq % Hkv == 0, and Tq <= Tk when causal.  lse is [B][Hq][Tq]. */
+int fa_ref_attn_f64(const double* q, const double* k, const double* v,
+                    double* o, double* lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                    int causal, double scale);
+
+/* Selected rows of the general problem; rows[r] = (b*Hq + h)*Tq + i. */
+int fa_ref_attn_rows_f64(const double* q, const double* k, const double* v,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                         int causal, double scale,
+                         const int64_t* rows, int64_t n_rows,
+                         double* o_rows, double* lse_rows);
+
 /* Number of OpenMP threads the oracle runs with. */
 int fa_ref_num_threads(void);
 
