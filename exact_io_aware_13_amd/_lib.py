@@ -24,7 +24,8 @@ FA_ERR_OVERFLOW = 6
 FA_ERR_HIP = 7
 FA_ERR_ARG = 8
 
-EXPORTED = ("fa_fwd", "fa_status_string", "fa_hip_error_string")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
+            "fa_status_string", "fa_hip_error_string")
 
 _lib = None
 
@@ -46,6 +47,15 @@ def load() -> ctypes.CDLL:
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
         lib.fa_fwd.restype = ctypes.c_int
+        lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
+        lib.fa_fwd_gqa.restype = ctypes.c_int
+        lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_float, i64, vp, ctypes.c_size_t, vp]
+        lib.fa_fwd_split.restype = ctypes.c_int
+        lib.fa_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+        lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+        lib.fa_fwd_split_count.restype = ctypes.c_int64
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_hip_error_string.argtypes = []
@@ -63,6 +73,29 @@ def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
     """Call ``fa_fwd`` with raw addresses; returns the fa_status code."""
     return int(load().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, T, d, int(causal),
                              float(scale), stream))
+
+
+def fa_fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
+                   T: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Call ``fa_fwd_gqa`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, T, d, int(causal),
+                                 float(scale), stream))
+
+
+def fa_fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
+                     Tq: int, Tk: int, d: int, causal: int, scale: float, n_split: int, ws_ptr: int,
+                     ws_bytes: int, stream: int) -> int:
+    """Call ``fa_fwd_split`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
+                                   float(scale), n_split, ws_ptr, ws_bytes, stream))
+
+
+def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: int) -> int:
+    return int(load().fa_fwd_split_workspace_bytes(B, Hq, Tq, Tk, d, n_split))
+
+
+def split_count(B: int, Hq: int, Tq: int, Tk: int, d: int, causal: bool) -> int:
+    return int(load().fa_fwd_split_count(B, Hq, Tq, Tk, d, int(bool(causal))))
 
 
 def _check(status: int) -> None:
@@ -86,40 +119,71 @@ def _check_tensors(q, k, v):
             raise ValueError(f"{name} must have shape (B, H, T, d), got {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.shape != v.shape:
+        raise ValueError(f"k, v shapes differ: {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q {tuple(q.shape)} and k/v {tuple(k.shape)} differ in batch or head size")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
 
 
-def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None) -> None:
-    """Exact attention forward into caller buffers ``o`` (bf16, like q) and ``lse`` (fp32, (B,H,T))."""
-    import torch
-    _check_tensors(q, k, v)
-    B, H, T, d = q.shape
-    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
-        raise ValueError("o must be a contiguous bf16 tensor shaped like q on q's device")
-    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 tensor of shape (B, H, T) on q's device")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          B, H, T, d, int(bool(causal)), float(scale), stream))
+def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: int | None = 1,
+            workspace=None) -> None:
+    """Exact attention forward into caller buffers ``o`` (bf16, like q) and ``lse`` (fp32, (B, Hq, Tq)).
 
-
-def fwd(q, k, v, causal: bool, scale: float | None = None):
-    """Exact attention forward; returns ``(o, lse)``.
-
-    ``q, k, v``: contiguous bf16 GPU tensors of shape (B, H, T, d), d in {64, 128}.
-    ``scale`` defaults to 1/sqrt(d).  ``o`` is bf16 like ``q``; ``lse`` is
-    float32 (B, H, T) in natural-log units.
+    ``q``: (B, Hq, Tq, d); ``k, v``: (B, Hkv, Tk, d).  One key/value head per
+    query head with Tq == Tk and one split calls ``fa_fwd``; grouped heads call
+    ``fa_fwd_gqa``; anything else (Tq != Tk, or ``n_split`` != 1; ``None`` asks
+    the library for a split count) calls ``fa_fwd_split``.  A split forward
+    needs ``workspace`` (a uint8 GPU tensor of ``split_workspace_bytes`` bytes);
+    if it is not given, one is allocated here.
     """
     import torch
     _check_tensors(q, k, v)
-    B, H, T, d = q.shape
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q on q's device")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Tq) on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_split is None:
+        n_split = split_count(B, Hq, Tq, Tk, d, causal)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if Tq == Tk and n_split == 1:
+            if Hkv == Hq:
+                st = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, Hq, Tq, d, int(bool(causal)), float(scale), stream)
+            else:
+                st = fa_fwd_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    B, Hq, Hkv, Tq, d, int(bool(causal)), float(scale), stream)
+        else:
+            need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split)
+            if workspace is None and need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr = workspace.data_ptr() if workspace is not None else 0
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), int(n_split),
+                                  ws_ptr, ws_bytes, stream)
+        _check(st)
+
+
+def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None = 1):
+    """Exact attention forward; returns ``(o, lse)``.
+
+    ``q``: contiguous bf16 GPU tensor (B, Hq, Tq, d); ``k, v``: (B, Hkv, Tk, d),
+    d in {64, 128}, Hq a multiple of Hkv.  ``scale`` defaults to 1/sqrt(d).
+    With ``causal`` the queries are the last Tq positions (query i sees keys
+    j <= i + Tk - Tq).  ``o`` is bf16 like ``q``; ``lse`` is float32
+    (B, Hq, Tq) in natural-log units.  ``n_split`` as in ``fwd_out``.
+    """
+    import torch
+    _check_tensors(q, k, v)
+    B, Hq, Tq, d = q.shape
     o = torch.empty_like(q)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    fwd_out(q, k, v, o, lse, causal, scale)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    fwd_out(q, k, v, o, lse, causal, scale, n_split)
     return o, lse

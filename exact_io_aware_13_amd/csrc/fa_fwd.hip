@@ -60,6 +60,7 @@
 //     causal query tiles go first.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -186,14 +187,37 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float m_new) {
 }
 
 
+// Launch arguments.  Query head h of batch b reads key/value head
+// b * (hq / group) + h / group.  The query rows are the last tq positions of
+// a tk-long sequence (causal: query i sees keys j <= i + tk - tq).  Key range
+// [s * chunk, (s + 1) * chunk) goes to split s; with SPLIT the workgroup
+// writes that split's normalised fp32 output and log-sum-exp to op / lp.
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    float* op;     // [n_split][rows][D]
+    float* lp;     // [n_split][rows]
+    long long rows;   // B * hq * tq
+    int tq, tk, n_qt, total, hq, group, chunk, n_split;
+    float c;       // scale * log2(e)
+};
+
 // One workgroup's work; `lds` is the workgroup's Geo<D, NG>::kLdsBytes of LDS.
-template <int D, bool CAUSAL, int NG>
+// The pointers come in as __restrict__ parameters (not through `a`): their
+// no-alias scopes also tell the compiler that the LDS reads of one tile do
+// not wait on the LDS DMA of another.
+template <int D, bool CAUSAL, int NG, bool SPLIT>
 __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                             float* __restrict__ LSE, int T, int n_qt, int total, float c_in,
-                                             FA_LDS char* const lds) {
+                                             float* __restrict__ LSE, float* __restrict__ OP,
+                                             float* __restrict__ LP, const FwdArgs& a, FA_LDS char* const lds) {
     using G = Geo<D, NG>;
     constexpr int kBM = G::kBM;
+    const int Tq = a.tq, Tk = a.tk, n_qt = a.n_qt, total = a.total;
+    const float c_in = a.c;
     FA_LDS char* const kslot[2] = {lds, lds + G::kTileBytes};
     FA_LDS char* const vslot[2] = {lds + 2 * G::kTileBytes, lds + 3 * G::kTileBytes};
 
@@ -208,30 +232,41 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     const int xcd = id % kXcds, xslot = id / kXcds;
     const int q8 = total / kXcds, r8 = total % kXcds;
     const int w = xcd < r8 ? xcd * (q8 + 1) + xslot : r8 * (q8 + 1) + (xcd - r8) * q8 + xslot;
-    int bh = w / n_qt;
+    int bh = w / (n_qt * a.n_split);
+    const int split = (w / n_qt) % a.n_split;
     int qt = CAUSAL ? n_qt - 1 - (w % n_qt) : (w % n_qt);
     // Causal work with few workgroups per CU (at most 8 rounds of the 256 CUs)
     // is tail-bound: when every XCD owns whole heads, its heads are walked
     // query-tile-major, so the heaviest tiles of all of them go first.  Longer
     // grids keep the head-major order, which keeps one head's K/V in L2.
     constexpr int kRoundSlots = 256 * (NG == 2 ? 1 : 2);   // CUs x workgroups per CU
-    if (CAUSAL && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
+    if (CAUSAL && a.n_split == 1 && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
         const int hx = q8 / n_qt;                 // heads per XCD
         bh = xcd * hx + xslot % hx;
         qt = n_qt - 1 - xslot / hx;
     }
 
-    const size_t base = (size_t)bh * (size_t)T * D;
-    const uint16_t* __restrict__ kbh = K + base;
-    const uint16_t* __restrict__ vbh = V + base;
-    const uint32_t head_bytes = (uint32_t)T * G::kRowBytes;
+    const int kvh = (bh / a.hq) * (a.hq / a.group) + (bh % a.hq) / a.group;   // key/value head
+    const size_t qbase = (size_t)bh * (size_t)Tq * D;
+    const size_t kvbase = (size_t)kvh * (size_t)Tk * D;
+    const uint16_t* __restrict__ kbh = K + kvbase;
+    const uint16_t* __restrict__ vbh = V + kvbase;
+    const uint32_t q_bytes = (uint32_t)Tq * G::kRowBytes;
 
-    const int qw0 = qt * kBM + wave * 32;   // first query row of this wave
+    const int blk = NG == 2 ? 2 * (wave & 3) + grp : wave;   // the two waves of a SIMD take adjacent row blocks
+    const int qw0 = qt * kBM + blk * 32;   // first query row of this wave
     const int qrow = qw0 + col;
-    const int n_all = (T + kBN - 1) / kBN;
-    const int kv_end = CAUSAL ? min(T, qt * kBM + kBM) : T;
-    const int n_kt = (kv_end + kBN - 1) / kBN;                       // tiles the workgroup loads
-    const int n_w = qw0 >= T ? 0 : (CAUSAL ? min(n_all, (qw0 + 31) / kBN + 1) : n_all);  // tiles this wave uses
+    // Keys of this split, [k_lo, k_hi); causal query i sees keys <= i + off.
+    const int off = Tk - Tq;
+    const int k_lo = split * a.chunk;
+    const int k_hi = min(Tk, k_lo + a.chunk);
+    const int kv_end = CAUSAL ? min(k_hi, min(Tq, qt * kBM + kBM) + off) : k_hi;
+    const int n_kt = kv_end > k_lo ? (kv_end - k_lo + kBN - 1) / kBN : 0;   // tiles the workgroup loads
+    const int w_end = CAUSAL ? min(k_hi, qw0 + 32 + off) : k_hi;            // keys this wave may see
+    const int n_w = qw0 >= Tq || w_end <= k_lo ? 0 : (w_end - k_lo + kBN - 1) / kBN;   // tiles it uses
+    // Tiles from j_mask on can hold keys some row of the wave must not see
+    // (past its diagonal, or past the split): at most the last two.
+    const int j_mask = CAUSAL ? min(n_w - 1, max(0, (qw0 + off + 1 - k_lo) / kBN)) : n_w - 1;
 
     // Per-lane byte offsets of this lane's 16-byte chunk in each tile load; the
     // wave's 1 KB blocks of a tile are contiguous in LDS.
@@ -243,7 +278,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         goff[c] = r * G::kRowBytes + 16 * (p ^ swz<D>(r));
     }
     auto load_tile = [&] __device__ (const uint16_t* src, int key0, FA_LDS char* slot) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (size_t)key0 * D, (uint32_t)(T - key0) * G::kRowBytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (size_t)key0 * D, (uint32_t)(Tk - key0) * G::kRowBytes);
 #pragma unroll
         for (int c = 0; c < G::kLoads; ++c)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(slot + (wave * G::kLoads + c) * 1024), 16,
@@ -269,12 +304,12 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             }
     }
 
-    load_tile(kbh, 0, kslot[0]);   // K_0; K_1 and V_0 follow in phase 0
+    if (n_kt > 0) load_tile(kbh, k_lo, kslot[0]);   // K_0; K_1 and V_0 follow in phase 0
 
     // Q^T operand (B operand of S^T): lane holds Q[qrow][16 s + 8 half .. +7]; zeros past T.
     bf16x8 qf[G::kDSteps];
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, head_bytes);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qbase, q_bytes);
         const uint32_t neg = c_in < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
         for (int s = 0; s < G::kDSteps; ++s) {
@@ -381,14 +416,14 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     // the same path (a single code path keeps the O accumulator in place).
     auto softmax_phase = [&] __device__ (int j) {
         if (j < 0 || j >= n_w) return;
-        if (j == n_w - 1) {
-            const int key0 = j * kBN;
+        if (j >= j_mask) {
+            const int key0 = k_lo + j * kBN;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool vis = key < T && (!CAUSAL || key <= qrow);
+                    const bool vis = key < k_hi && (!CAUSAL || key <= qrow + off);
                     sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
                 }
         }
@@ -433,8 +468,8 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             const int j = ph >> 1;
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loads of phase ph - 2 have landed
             __syncthreads();
-            if (j + 1 < n_kt) load_tile(kbh, (j + 1) * kBN, kslot[(j + 1) & 1]);
-            if (j < n_kt) load_tile(vbh, j * kBN, vslot[j & 1]);
+            if (j + 1 < n_kt) load_tile(kbh, k_lo + (j + 1) * kBN, kslot[(j + 1) & 1]);
+            if (j < n_kt) load_tile(vbh, k_lo + j * kBN, vslot[j & 1]);
         }
     };
     // Each group runs its own straight-line loop; both loops pass the same
@@ -472,38 +507,90 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         }
     }
 
-    // Epilogue: O = o / l (bf16, round to nearest even), lse = ln2 * (m + log2 l).
+    // Epilogue: O = o / l, lse = ln2 * (m + log2 l).  A row that saw no key
+    // (possible only for one split of a split problem) gets O = 0, lse = -inf.
     const float l32 = xhalf_sum(st.l32);
     const float l16 = xhalf_sum(st.l16);
-    if (n_w == 0) return;
-    const float inv = 1.0f / l16;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + base, head_bytes);   // rows past T are dropped
-    const uint32_t orow = (uint32_t)qrow * G::kRowBytes;
+    const float inv = l16 > 0.0f ? 1.0f / l16 : 0.0f;
+    const float lse_row = kLn2 * (st.m + __builtin_amdgcn_logf(l32));
+    if constexpr (!SPLIT) {
+        if (n_w == 0) return;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + qbase, q_bytes);   // rows past Tq are dropped
+        const uint32_t orow = (uint32_t)qrow * G::kRowBytes;
 #pragma unroll
-    for (int b = 0; b < G::kDBlocks; ++b)
+        for (int b = 0; b < G::kDBlocks; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            u32x2 wv;
-            wv.x = pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv);
-            wv.y = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
-            __builtin_amdgcn_raw_buffer_store_b64(wv, ro, orow + 2 * (b * 32 + 8 * g + 4 * half), 0, 0);
+            for (int g = 0; g < 4; ++g) {
+                u32x2 wv;
+                wv.x = pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv);
+                wv.y = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(wv, ro, orow + 2 * (b * 32 + 8 * g + 4 * half), 0, 0);
+            }
+        if (half == 0) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)bh * Tq, (uint32_t)Tq * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
         }
-    if (half == 0) {
-        const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)bh * T, (uint32_t)T * 4u);
-        __builtin_amdgcn_raw_buffer_store_b32(as_u32(kLn2 * (st.m + __builtin_amdgcn_logf(l32))), rl,
-                                              (uint32_t)qrow * 4u, 0, 0);
+    } else {
+        // Every row of the split is written, also those that saw no key.
+        const size_t prow = (size_t)split * (size_t)a.rows + (size_t)bh * Tq;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(OP + prow * D, (uint32_t)Tq * D * 4u);
+        const uint32_t orow = (uint32_t)qrow * D * 4u;
+#pragma unroll
+        for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x4 wv = {as_u32(st.o[b][4 * g + 0] * inv), as_u32(st.o[b][4 * g + 1] * inv),
+                            as_u32(st.o[b][4 * g + 2] * inv), as_u32(st.o[b][4 * g + 3] * inv)};
+                __builtin_amdgcn_raw_buffer_store_b128(wv, ro, orow + 4 * (b * 32 + 8 * g + 4 * half), 0, 0);
+            }
+        if (half == 0) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(LP + prow, (uint32_t)Tq * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+        }
     }
 }
 
 // Two waves per SIMD: NG = 2 is one 8-wave workgroup per CU whose wave groups
 // alternate phases; NG = 1 is two independent 4-wave workgroups per CU.
-template <int D, bool CAUSAL, int NG>
+template <int D, bool CAUSAL, int NG, bool SPLIT>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                   int T, int n_qt, int total, float c_in /* scale * log2(e) */) {
+void fa_fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[Geo<D, NG>::kLdsBytes];
-    fa_fwd_block<D, CAUSAL, NG>(Q, K, V, O, LSE, T, n_qt, total, c_in, (FA_LDS char*)smem);
+    fa_fwd_block<D, CAUSAL, NG, SPLIT>(a.q, a.k, a.v, a.o, a.lse, a.op, a.lp, a, (FA_LDS char*)smem);
+}
+
+// Merge of the splits' partial results, the log-sum-exp combine of "FlashAttention
+// and Fused Kernels: Attention Without the n x n Matrix", Step 4: with M the
+// largest split lse, w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
+// lse = M + ln sum_s w_s.  D / 4 lanes per row, four values each; a split
+// that saw no key (lse_s = -inf) gets weight zero.
+template <int D>
+__global__ __launch_bounds__(256) void fa_combine_kernel(const float* __restrict__ op, const float* __restrict__ lp,
+                                                         uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                         long long rows, int n_split) {
+    constexpr int kLanes = D / 4;
+    constexpr int kRowsPerBlock = 256 / kLanes;
+    const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
+    const int t = threadIdx.x % kLanes;
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int s = 0; s < n_split; ++s) m = fmaxf(m, lp[(size_t)s * rows + row]);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float l = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+        const float ls = lp[(size_t)s * rows + row];
+        const float w = ls == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((ls - m) * (float)kLog2e);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(op + ((size_t)s * rows + row) * D + 4 * t);
+        l += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, as_f32(raw[e]), acc[e]);
+    }
+    const float inv = 1.0f / l;
+    u32x2 wv;
+    wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(o + (size_t)row * D + 4 * t) = wv;
+    if (t == 0) lse[row] = m + kLn2 * __builtin_amdgcn_logf(l);
 }
 
 thread_local char g_hip_error[256] = "";
@@ -513,26 +600,39 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <int D, bool CAUSAL, int NG>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int T, int n_qt, int total,
-                  float c, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, NG>), dim3(total), dim3(Geo<D, NG>::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, T, n_qt, total, c);
+template <int D, bool CAUSAL, int NG, bool SPLIT>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, NG, SPLIT>), dim3(a.total), dim3(Geo<D, NG>::kThreads), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int D, bool SPLIT>
+hipError_t launch_d(const FwdArgs& a, bool causal, int ng, hipStream_t stream) {
+    if (ng == 2) return causal ? launch<D, true, 2, SPLIT>(a, stream) : launch<D, false, 2, SPLIT>(a, stream);
+    return causal ? launch<D, true, 1, SPLIT>(a, stream) : launch<D, false, 1, SPLIT>(a, stream);
+}
 
-extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                            int64_t H, int64_t T, int64_t d, int causal, float scale, hipStream_t stream) {
+// Keys per split: the split count spread evenly, rounded up to whole key tiles.
+int64_t split_chunk(int64_t Tk, int64_t n_split) {
+    const int64_t per = (Tk + n_split - 1) / n_split;
+    return (per + kBN - 1) / kBN * kBN;
+}
+
+// The general forward behind every entry point.
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                  int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale, int64_t n_split,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B < 1 || H < 1 || T < 1) return FA_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (causal && Tq > Tk) return FA_ERR_SHAPE;
+    if (n_split < 1) return FA_ERR_ARG;
     if (!std::isfinite(scale)) return FA_ERR_SCALE;
     const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
-    if ((addr(q) | addr(k) | addr(v) | addr(o)) & 15u) return FA_ERR_ALIGN;
+    if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(workspace)) & 15u) return FA_ERR_ALIGN;
     if (addr(lse) & 3u) return FA_ERR_ALIGN;
 
     // Workgroup shape: the phase-alternating 8-wave workgroup pays off when
@@ -542,48 +642,75 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
 #ifndef FA_FORCE_GROUPS
 #define FA_FORCE_GROUPS 0
 #endif
-    const int ng = FA_FORCE_GROUPS ? FA_FORCE_GROUPS : (d == 128 && T * (causal ? 1 : 2) >= 8192 ? 2 : 1);
+    const int ng = FA_FORCE_GROUPS ? FA_FORCE_GROUPS : (d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1);
     const int64_t bm = 128 * ng;
 
-    // Sizes: every byte count must fit int64; in-kernel row indices are 32-bit.
+    // Sizes: every byte count must fit int64; in-kernel row and key indices are 32-bit.
     const int64_t kMax = INT64_MAX;
-    if (B > kMax / H) return FA_ERR_OVERFLOW;
-    const int64_t BH = B * H;
-    if (BH > kMax / T) return FA_ERR_OVERFLOW;
-    const int64_t rows = BH * T;
-    if (rows > kMax / (2 * d)) return FA_ERR_OVERFLOW;
-    if (T > INT32_MAX - 2 * bm) return FA_ERR_OVERFLOW;
-    // Buffer descriptors address one head: (T + 2 query tiles) rows must fit in 32-bit byte offsets.
-    if ((T + 2 * bm) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
-    const int64_t n_qt = (T + bm - 1) / bm;
-    if (BH > INT32_MAX / n_qt) return FA_ERR_OVERFLOW;
-    const int total = static_cast<int>(BH * n_qt);
+    if (B > kMax / Hq) return FA_ERR_OVERFLOW;
+    const int64_t BH = B * Hq, BHkv = B * Hkv;
+    if (BH > kMax / Tq || BHkv > kMax / Tk) return FA_ERR_OVERFLOW;
+    const int64_t rows = BH * Tq, kv_rows = BHkv * Tk;
+    if (rows > kMax / (4 * (d + 1)) || kv_rows > kMax / (2 * d)) return FA_ERR_OVERFLOW;
+    if (Tq > INT32_MAX - 2 * bm || Tk > INT32_MAX - 2 * bm) return FA_ERR_OVERFLOW;
+    // Buffer descriptors address one head: (T + 2 tiles) rows must fit in 32-bit byte offsets.
+    if ((Tq + 2 * bm) * 4 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
+    if ((Tk + 2 * bm) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
+    const int64_t chunk = split_chunk(Tk, n_split);
+    const int64_t n_eff = (Tk + chunk - 1) / chunk;   // splits that hold at least one key
+    const int64_t n_qt = (Tq + bm - 1) / bm;
+    if (BH > INT32_MAX / (n_qt * n_eff)) return FA_ERR_OVERFLOW;
 
-    const size_t tensor_bytes = static_cast<size_t>(rows) * static_cast<size_t>(d) * 2u;
+    const size_t q_bytes = static_cast<size_t>(rows) * static_cast<size_t>(d) * 2u;
+    const size_t kv_bytes = static_cast<size_t>(kv_rows) * static_cast<size_t>(d) * 2u;
     const size_t lse_bytes = static_cast<size_t>(rows) * 4u;
-    for (const void* in : {q, k, v}) {
-        if (overlaps(o, tensor_bytes, in, tensor_bytes)) return FA_ERR_ARG;
-        if (overlaps(lse, lse_bytes, in, tensor_bytes)) return FA_ERR_ARG;
+    const size_t ws_need = n_eff > 1 ? static_cast<size_t>(n_eff) * static_cast<size_t>(rows) * (d + 1) * 4u : 0;
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
+    const struct { const void* p; size_t n; } ins[3] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
+    for (const auto& in : ins) {
+        if (overlaps(o, q_bytes, in.p, in.n) || overlaps(lse, lse_bytes, in.p, in.n)) return FA_ERR_ARG;
+        if (ws_need && overlaps(workspace, ws_need, in.p, in.n)) return FA_ERR_ARG;
     }
-    if (overlaps(o, tensor_bytes, lse, lse_bytes)) return FA_ERR_ARG;
+    if (overlaps(o, q_bytes, lse, lse_bytes)) return FA_ERR_ARG;
+    if (ws_need && (overlaps(workspace, ws_need, o, q_bytes) || overlaps(workspace, ws_need, lse, lse_bytes)))
+        return FA_ERR_ARG;
 
-    const float c = static_cast<float>(static_cast<double>(scale) * kLog2e);
-    const int Ti = static_cast<int>(T), nq = static_cast<int>(n_qt);
+    FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.op = static_cast<float*>(workspace);
+    a.lp = ws_need ? static_cast<float*>(workspace) + static_cast<size_t>(n_eff) * rows * d : nullptr;
+    a.rows = rows;
+    a.tq = static_cast<int>(Tq);
+    a.tk = static_cast<int>(Tk);
+    a.n_qt = static_cast<int>(n_qt);
+    a.total = static_cast<int>(BH * n_qt * n_eff);
+    a.hq = static_cast<int>(Hq);
+    a.group = static_cast<int>(Hq / Hkv);
+    a.chunk = static_cast<int>(chunk);
+    a.n_split = static_cast<int>(n_eff);
+    a.c = static_cast<float>(static_cast<double>(scale) * kLog2e);
+
     hipError_t err;
-    if (d == 128) {
-        if (ng == 2)
-            err = causal ? launch<128, true, 2>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                         : launch<128, false, 2>(q, k, v, o, lse, Ti, nq, total, c, stream);
-        else
-            err = causal ? launch<128, true, 1>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                         : launch<128, false, 1>(q, k, v, o, lse, Ti, nq, total, c, stream);
+    if (n_eff == 1) {
+        err = d == 128 ? launch_d<128, false>(a, causal, ng, stream) : launch_d<64, false>(a, causal, ng, stream);
     } else {
-        if (ng == 2)
-            err = causal ? launch<64, true, 2>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                         : launch<64, false, 2>(q, k, v, o, lse, Ti, nq, total, c, stream);
-        else
-            err = causal ? launch<64, true, 1>(q, k, v, o, lse, Ti, nq, total, c, stream)
-                         : launch<64, false, 1>(q, k, v, o, lse, Ti, nq, total, c, stream);
+        err = d == 128 ? launch_d<128, true>(a, causal, ng, stream) : launch_d<64, true>(a, causal, ng, stream);
+        if (err == hipSuccess) {
+            const int rpb = static_cast<int>(256 / (d / 4));
+            const int64_t blocks = (rows + rpb - 1) / rpb;
+            if (blocks > INT32_MAX) return FA_ERR_OVERFLOW;
+            if (d == 128)
+                hipLaunchKernelGGL(fa_combine_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                                   a.op, a.lp, a.o, lse, rows, a.n_split);
+            else
+                hipLaunchKernelGGL(fa_combine_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                                   a.op, a.lp, a.o, lse, rows, a.n_split);
+            err = hipGetLastError();
+        }
     }
     if (err != hipSuccess) {
         std::snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(err), hipGetErrorString(err));
@@ -593,17 +720,60 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     return FA_OK;
 }
 
+}  // namespace
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                            int64_t H, int64_t T, int64_t d, int causal, float scale, hipStream_t stream) {
+    return run_fwd(q, k, v, o, lse, B, H, H, T, T, d, causal, scale, 1, nullptr, 0, stream);
+}
+
+extern "C" fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t T, int64_t d, int causal, float scale,
+                                hipStream_t stream) {
+    return run_fwd(q, k, v, o, lse, B, Hq, Hkv, T, T, d, causal, scale, 1, nullptr, 0, stream);
+}
+
+extern "C" size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
+                                               int64_t n_split) {
+    if (B < 1 || Hq < 1 || Tq < 1 || Tk < 1 || d < 1 || n_split < 1) return 0;
+    const int64_t chunk = split_chunk(Tk, n_split);
+    const int64_t n_eff = (Tk + chunk - 1) / chunk;
+    if (n_eff == 1) return 0;
+    const double bytes = (double)n_eff * (double)B * (double)Hq * (double)Tq * (double)(d + 1) * 4.0;
+    if (bytes > 9.0e18) return 0;
+    return static_cast<size_t>(n_eff * B * Hq * Tq * (d + 1) * 4);
+}
+
+extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d, int causal) {
+    if (B < 1 || Hq < 1 || Tq < 1 || Tk < 1 || (d != 64 && d != 128)) return 1;
+    const int64_t ng = d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1;
+    const int64_t slots = 256 * (ng == 2 ? 1 : 2);            // CUs x resident workgroups per CU
+    const int64_t wgs = B * Hq * ((Tq + 128 * ng - 1) / (128 * ng));
+    if (wgs >= slots) return 1;
+    int64_t n = (2 * slots + wgs - 1) / wgs;                   // about two rounds of workgroups
+    n = std::min<int64_t>(n, std::max<int64_t>(1, Tk / 128));  // at least two key tiles per split
+    return std::min<int64_t>(n, 64);
+}
+
+extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                  int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal,
+                                  float scale, int64_t n_split, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    return run_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split, workspace, workspace_bytes,
+                   stream);
+}
+
 extern "C" const char* fa_status_string(fa_status status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
-        case FA_ERR_SHAPE: return "B, H and T must all be >= 1";
+        case FA_ERR_SHAPE: return "sizes must be >= 1, Hq a multiple of Hkv, and Tq <= Tk when causal";
         case FA_ERR_HEAD_DIM: return "head size d must be 64 or 128";
         case FA_ERR_SCALE: return "scale must be finite";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case FA_ERR_OVERFLOW: return "sizes overflow the supported index range";
         case FA_ERR_HIP: return "HIP kernel launch failed";
-        case FA_ERR_ARG: return "causal must be 0 or 1, and outputs must not overlap inputs";
+        case FA_ERR_ARG: return "bad argument: causal not 0/1, n_split < 1, workspace too small, or overlapping buffers";
     }
     return "unknown status";
 }

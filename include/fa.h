@@ -23,6 +23,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -33,14 +34,16 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
-    FA_ERR_SHAPE = 2,     /* B, H or T < 1                                       */
+    FA_ERR_SHAPE = 2,     /* a size < 1, Hq not a multiple of Hkv, or causal with
+                             Tq > Tk                                             */
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte   */
     FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid,
                              or one head (T*d*2 bytes plus 2 row tiles) >= 4 GiB */
     FA_ERR_HIP = 7,       /* the kernel launch failed; see fa_hip_error_string()  */
-    FA_ERR_ARG = 8        /* causal not 0/1, or an output overlaps an input       */
+    FA_ERR_ARG = 8        /* causal not 0/1, n_split < 1, workspace too small, or
+                             overlapping buffers                                 */
 } fa_status;
 
 /*
@@ -74,6 +77,65 @@ fa_status fa_fwd(const void* q, const void* k, const void* v,
                  void* o, float* lse,
                  int64_t B, int64_t H, int64_t T, int64_t d,
                  int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_gqa -- fa_fwd with grouped key/value heads.
+ *
+ * Llama 3.1 8B shares each key/value head among four query heads
+ * ("FlashAttention and Fused Kernels: Attention Without the n x n Matrix",
+ * Step 4).  Here q and o are [B][Hq][T][d], k and v are [B][Hkv][T][d], and
+ * query head h reads key/value head h / (Hq / Hkv): consecutive query heads
+ * share one.  Hq must be a multiple of Hkv (else FA_ERR_SHAPE); Hkv == Hq is
+ * fa_fwd.  Everything else (layout, lse, ownership, errors) is as for fa_fwd.
+ */
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v,
+                     void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t d,
+                     int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_split -- the general forward, with the keys split across workgroups.
+ *
+ * This is Flash-Decoding ("FlashAttention and Fused Kernels: Attention Without
+ * the n x n Matrix", Step 4).  The keys are cut into n_split contiguous
+ * chunks of whole 64-key tiles, each chunk is attended by its own
+ * workgroups, and a second kernel merges the chunks with the log-sum-exp
+ * combine of the same step.  This gives a short query block (decode: Tq = 1)
+ * against a long cache enough parallel work.
+ *
+ * q, o    : bf16 [B][Hq][Tq][d];  k, v : bf16 [B][Hkv][Tk][d];  lse : fp32
+ *           [B][Hq][Tq].  Hq a multiple of Hkv; head mapping as fa_fwd_gqa.
+ * causal  : the query rows are the last Tq positions of the Tk-long sequence,
+ *           so query i sees keys j <= i + (Tk - Tq).  This needs Tq <= Tk
+ *           (else FA_ERR_SHAPE).  Without causal, Tq and Tk are free.
+ * n_split : >= 1.  Chunks are ceil(Tk / n_split) keys, rounded up to a
+ *           multiple of 64, so fewer chunks than asked may exist.  When one
+ *           chunk results, no workspace is used and no combine runs.
+ * workspace, workspace_bytes : device scratch owned by the caller, 16-byte
+ *           aligned, at least fa_fwd_split_workspace_bytes(...) bytes.  It holds
+ *           each chunk's fp32 output and log-sum-exp.  It may be NULL when
+ *           that size is 0; it must not overlap any other buffer.
+ *
+ * The workspace is overwritten on every call; calls that share it must not
+ * run concurrently.  The two kernels are enqueued in order on `stream`.
+ * Errors as fa_fwd, plus: FA_ERR_NULL for a missing workspace, and
+ * FA_ERR_ARG for n_split < 1, a workspace that is too small, or overlaps.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v,
+                       void* o, float* lse,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                       int causal, float scale, int64_t n_split,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fa_fwd_split needs for these sizes (0: none needed, or
+ * invalid sizes). */
+size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
+                                    int64_t n_split);
+
+/* A split count that gives the GPU enough workgroups for these sizes (1
+ * when the query tiles alone fill it).  Advice only; any n_split >= 1 is
+ * valid. */
+int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d, int causal);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status status);

@@ -115,3 +115,59 @@ def test_python_wrapper_rejects_cpu_tensors():
         fa.fwd(x, x, x, True)
     with pytest.raises(ValueError):
         fa.fwd(x.float(), x, x, True)
+
+
+def call_gqa(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, Hq=4, Hkv=2, T=16, d=64, causal=1, scale=0.125):
+    return _lib.fa_fwd_gqa_raw(q, k, v, o, lse, B, Hq, Hkv, T, d, causal, scale, 0)
+
+
+def call_split(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, Hq=4, Hkv=2, Tq=4, Tk=1024, d=64, causal=1,
+               scale=0.125, n_split=4, ws=16 * A, ws_bytes=1 << 30):
+    return _lib.fa_fwd_split_raw(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split, ws, ws_bytes, 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 3), (2, 4), (4, 0), (0, 1), (6, 4)])
+def test_gqa_bad_head_counts(lib, Hq, Hkv):
+    assert call_gqa(Hq=Hq, Hkv=Hkv) == _lib.FA_ERR_SHAPE
+
+
+def test_gqa_other_checks(lib):
+    assert call_gqa(k=0) == _lib.FA_ERR_NULL
+    assert call_gqa(d=96) == _lib.FA_ERR_HEAD_DIM
+    assert call_gqa(v=3 * A + 8) == _lib.FA_ERR_ALIGN
+    assert call_gqa(scale=math.nan) == _lib.FA_ERR_SCALE
+
+
+def test_split_shape_rules(lib):
+    assert call_split(Tq=2048, Tk=1024, causal=1) == _lib.FA_ERR_SHAPE      # causal needs Tq <= Tk
+    assert call_split(Tq=0) == _lib.FA_ERR_SHAPE
+    assert call_split(Tk=0) == _lib.FA_ERR_SHAPE
+    assert call_split(Hq=6, Hkv=4) == _lib.FA_ERR_SHAPE
+
+
+def test_split_workspace_rules(lib):
+    assert call_split(n_split=0) == _lib.FA_ERR_ARG
+    assert call_split(n_split=-3) == _lib.FA_ERR_ARG
+    assert call_split(ws=0, ws_bytes=0) == _lib.FA_ERR_NULL                  # 4 splits need scratch
+    need = _lib.split_workspace_bytes(1, 4, 4, 1024, 64, 4)
+    assert call_split(ws_bytes=need - 4) == _lib.FA_ERR_ARG
+    assert call_split(ws=16 * A + 4) == _lib.FA_ERR_ALIGN
+    assert call_split(ws=A) == _lib.FA_ERR_ARG                               # workspace over q
+
+
+def test_split_workspace_bytes(lib):
+    # four chunks of 256 keys: 4 x (B Hq Tq) rows x (d + 1) floats
+    assert _lib.split_workspace_bytes(1, 4, 4, 1024, 64, 4) == 4 * 16 * 65 * 4
+    # chunks round up to whole 64-key tiles: 100 keys in 7 splits is two chunks of 64
+    assert _lib.split_workspace_bytes(2, 3, 5, 100, 128, 7) == 2 * (2 * 3 * 5) * 129 * 4
+    # one chunk: no workspace
+    assert _lib.split_workspace_bytes(1, 1, 1, 64, 64, 8) == 0
+    assert _lib.split_workspace_bytes(1, 1, 1, 1000, 64, 1) == 0
+    assert _lib.split_workspace_bytes(0, 1, 1, 1000, 64, 2) == 0
+
+
+def test_split_count_advice(lib):
+    assert _lib.split_count(1, 32, 1, 32768, 128, True) > 1           # decode: one row per head
+    assert _lib.split_count(1, 32, 8192, 8192, 128, True) == 1        # prefill fills the GPU
+    assert _lib.split_count(1, 1, 1, 64, 64, False) == 1              # a single tile cannot split
+    assert 1 <= _lib.split_count(1, 8, 1, 1 << 20, 64, False) <= 64

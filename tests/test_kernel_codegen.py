@@ -1,0 +1,54 @@
+"""The generated gfx950 code of every forward kernel, checked on the host.
+
+hipcc cross-compiles the device code to assembly (no GPU needed), and the
+checks guard properties that decide the kernel's speed but no numerics test
+sees:
+  * no register spills (scratch traffic in the inner loop);
+  * no wait on the tile loads (vmcnt) right before an LDS read: the tile loads
+    write LDS directly, and a read of one tile must not wait for the load of
+    the next, which would put the HBM latency back on every tile.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_13_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "fa_fwd.s"
+    cmd = [build.hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + \
+        ["--cuda-device-only", "-S", "-o", str(out), build.SRC]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(asm):
+    for m in re.finditer(r"^(_ZN\S*fa_fwd_kernel\S*):", asm, re.M):
+        start = m.end()
+        end = asm.index(".Lfunc_end", start)
+        body = [l.strip() for l in asm[start:end].splitlines()]
+        yield m.group(1), [l for l in body if l and not l.startswith((";", "."))]
+
+
+def test_every_variant_is_compiled(asm):
+    names = [n for n, _ in _kernels(asm)]
+    assert len(names) == 16, names      # d x causal x wave groups x split
+
+
+def test_no_register_spills(asm):
+    spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)]
+    sgpr_spills = [int(x) for x in re.findall(r"\.sgpr_spill_count:\s+(\d+)", asm)]
+    assert spills and max(spills) == 0 and max(sgpr_spills) == 0
+
+
+def test_lds_reads_do_not_wait_on_tile_loads(asm):
+    for name, body in _kernels(asm):
+        waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
+                 if a.startswith("s_waitcnt") and "vmcnt" in a and b.startswith("ds_read")]
+        assert not waits, (name, [body[i:i + 2] for i in waits[:3]])
