@@ -54,7 +54,7 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_split.restype = ctypes.c_int
         lib.fa_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
-        lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+        lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
         lib.fa_fwd_split_count.restype = ctypes.c_int64
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
@@ -94,8 +94,8 @@ def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: in
     return int(load().fa_fwd_split_workspace_bytes(B, Hq, Tq, Tk, d, n_split))
 
 
-def split_count(B: int, Hq: int, Tq: int, Tk: int, d: int, causal: bool) -> int:
-    return int(load().fa_fwd_split_count(B, Hq, Tq, Tk, d, int(bool(causal))))
+def split_count(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: bool) -> int:
+    return int(load().fa_fwd_split_count(B, Hq, Hkv, Tq, Tk, d, int(bool(causal))))
 
 
 def _check(status: int) -> None:
@@ -149,7 +149,7 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if n_split is None:
-        n_split = split_count(B, Hq, Tq, Tk, d, causal)
+        n_split = split_count(B, Hq, Hkv, Tq, Tk, d, causal)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         if Tq == Tk and n_split == 1:

@@ -633,6 +633,17 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (!std::isfinite(scale)) return FA_ERR_SCALE;
     const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
     if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(workspace)) & 15u) return FA_ERR_ALIGN;
+
+    // Grouped heads whose rows all see the same keys (no mask, or one query
+    // row, which sees every key) are one problem per key/value head: the
+    // group's query rows [h0, h0 + group) x [0, Tq) are contiguous in q, o and
+    // lse, so they run as group * Tq query rows of that head, and each K/V
+    // tile is loaded once for the whole group.
+    if (Hq != Hkv && (!causal || Tq == 1)) {
+        Tq *= Hq / Hkv;
+        Hq = Hkv;
+        causal = 0;   // a single query row per head sees every key either way
+    }
     if (addr(lse) & 3u) return FA_ERR_ALIGN;
 
     // Workgroup shape: the phase-alternating 8-wave workgroup pays off when
@@ -744,8 +755,14 @@ extern "C" size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq
     return static_cast<size_t>(n_eff * B * Hq * Tq * (d + 1) * 4);
 }
 
-extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d, int causal) {
-    if (B < 1 || Hq < 1 || Tq < 1 || Tk < 1 || (d != 64 && d != 128)) return 1;
+extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                                      int causal) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tk < 1 || (d != 64 && d != 128)) return 1;
+    if (Hq != Hkv && (!causal || Tq == 1)) {   // folded as in the forward itself
+        Tq *= Hq / Hkv;
+        Hq = Hkv;
+        causal = 0;
+    }
     const int64_t ng = d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1;
     const int64_t slots = 256 * (ng == 2 ? 1 : 2);            // CUs x resident workgroups per CU
     const int64_t wgs = B * Hq * ((Tq + 128 * ng - 1) / (128 * ng));

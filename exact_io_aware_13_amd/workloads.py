@@ -38,24 +38,47 @@ class Workload:
     seed: int
     spikes: bool = False
     sampled_rows: bool = False   # parity on sampled rows instead of every row
+    hkv: int = 0                 # key/value heads (0: one per query head)
+    tk: int = 0                  # keys (0: T, the square problem)
+    n_split: int = 1             # key splits for the split forward (None: the library's advice)
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def Hkv(self) -> int:
+        return self.hkv or self.H
+
+    @property
+    def Tk(self) -> int:
+        return self.tk or self.T
+
+    @property
     def shape(self):
         return (self.B, self.H, self.T, self.d)
 
+    @property
+    def kv_shape(self):
+        return (self.B, self.Hkv, self.Tk, self.d)
+
     def flops(self) -> float:
-        """Attention FLOPs, 4*B*H*T^2*d, halved for causal (metric convention)."""
-        f = 4.0 * self.B * self.H * self.T * self.T * self.d
-        return f / 2.0 if self.causal else f
+        """Attention FLOPs: 4 d per visible (query, key) pair; for the square
+        problem 4*B*H*T^2*d, halved for causal (metric convention)."""
+        if self.Tk == self.T:
+            f = 4.0 * self.B * self.H * self.T * self.T * self.d
+            return f / 2.0 if self.causal else f
+        if not self.causal:
+            return 4.0 * self.B * self.H * self.T * self.Tk * self.d
+        off = self.Tk - self.T   # query i sees i + off + 1 keys
+        pairs = self.T * (off + 1) + self.T * (self.T - 1) / 2.0
+        return 4.0 * self.B * self.H * pairs * self.d
 
     def algorithmic_bytes(self) -> int:
         """One read of Q, K, V and one write of O (2 B/element) plus lse (4 B/row)."""
-        n = self.B * self.H * self.T
-        return 4 * n * self.d * 2 + 4 * n
+        nq = self.B * self.H * self.T
+        nkv = self.B * self.Hkv * self.Tk
+        return 2 * nq * self.d * 2 + 2 * nkv * self.d * 2 + 4 * nq
 
 
 WORKLOADS = [
@@ -68,6 +91,11 @@ WORKLOADS = [
              seed=4),
     Workload("c5", "long-context spiky causal prefill B=1 H=32 T=32768 d=128", 1, 32, 32768, 128, True,
              seed=5, spikes=True, sampled_rows=True),
+    # Llama 3.1 8B shares each key/value head among four query heads.
+    Workload("gqa", "Llama-3.1-8B GQA causal prefill B=1 Hq=32 Hkv=8 T=8192 d=128", 1, 32, 8192, 128, True,
+             seed=6, sampled_rows=True, hkv=8),
+    Workload("decode", "Llama-3.1-8B GQA decode B=8 Hq=32 Hkv=8 Tq=1 Tk=32768 d=128, split keys", 8, 32, 1, 128,
+             True, seed=7, hkv=8, tk=32768, n_split=None),
 ]
 BY_KEY = {w.key: w for w in WORKLOADS}
 
@@ -113,8 +141,18 @@ def draw_bf16(shape, seed: int, spikes: bool = False):
 
 
 def workload_inputs(w: Workload):
-    """The bf16 Q, K, V bits of a named workload."""
-    return draw_bf16(w.shape, w.seed, w.spikes)
+    """The bf16 Q, K, V bits of a named workload.
+
+    Square one-head-per-query-head workloads use ``draw_bf16``.  Others draw
+    Q (B, Hq, Tq, d), then K and V (B, Hkv, Tk, d), from one generator in that
+    order (no spikes)."""
+    if w.kv_shape == w.shape:
+        return draw_bf16(w.shape, w.seed, w.spikes)
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal(size=w.shape, dtype=np.float32)
+    k = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
+    v = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
 def spike_masks(shape, seed: int):

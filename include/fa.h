@@ -116,6 +116,10 @@ fa_status fa_fwd_gqa(const void* q, const void* k, const void* v,
  *           each chunk's fp32 output and log-sum-exp.  It may be NULL when
  *           that size is 0; it must not overlap any other buffer.
  *
+ * Grouped heads with no mask (or one query row per head) run as one problem
+ * per key/value head with Hq / Hkv * Tq query rows, so every key/value tile is
+ * read once per group rather than once per query head.
+ *
  * The workspace is overwritten on every call; calls that share it must not
  * run concurrently.  The two kernels are enqueued in order on `stream`.
  * Errors as fa_fwd, plus: FA_ERR_NULL for a missing workspace, and
@@ -135,7 +139,7 @@ size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t T
 /* A split count that gives the GPU enough workgroups for these sizes (1
  * when the query tiles alone fill it).  Advice only; any n_split >= 1 is
  * valid. */
-int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d, int causal);
+int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status status);

@@ -167,7 +167,10 @@ def test_split_workspace_bytes(lib):
 
 
 def test_split_count_advice(lib):
-    assert _lib.split_count(1, 32, 1, 32768, 128, True) > 1           # decode: one row per head
-    assert _lib.split_count(1, 32, 8192, 8192, 128, True) == 1        # prefill fills the GPU
-    assert _lib.split_count(1, 1, 1, 64, 64, False) == 1              # a single tile cannot split
-    assert 1 <= _lib.split_count(1, 8, 1, 1 << 20, 64, False) <= 64
+    assert _lib.split_count(1, 32, 32, 1, 32768, 128, True) > 1       # decode: one row per head
+    assert _lib.split_count(1, 32, 8, 8192, 8192, 128, True) == 1     # prefill fills the GPU
+    assert _lib.split_count(1, 1, 1, 1, 64, 64, False) == 1           # a single tile cannot split
+    assert 1 <= _lib.split_count(1, 8, 8, 1, 1 << 20, 64, False) <= 64
+    # grouped decode folds the group into rows: fewer workgroups, so more splits
+    assert _lib.split_count(8, 32, 8, 1, 32768, 128, True) > _lib.split_count(8, 32, 32, 1, 32768, 128, True)
+    assert _lib.split_count(1, 32, 33, 1, 4096, 128, True) == 1       # invalid grouping

@@ -138,3 +138,28 @@ def test_split_workspace_reuse_and_stream(fa):
         o_ref, l_ref = oracle.attention_f64(qb, kb, vb, True, 0.125)
         check(oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16)), o_ref,
               lse.cpu().numpy().astype(np.float64), l_ref, f"reuse Tq={Tq} Tk={Tk}")
+
+
+def test_workload_gqa_prefill_sampled_rows(fa):
+    """Llama-3.1-8B GQA causal prefill at T=8192: seeded sample rows against the oracle."""
+    w = wl.BY_KEY["gqa"]
+    say("case gqa:", w.title)
+    qb, kb, vb = wl.workload_inputs(w)
+    scale = np.float32(w.scale)
+    o, lse = run(fa, qb, kb, vb, w.causal, scale)
+    rows = wl.sample_rows(w)
+    o_ref, lse_ref = oracle.attention_rows_f64(qb, kb, vb, w.causal, float(scale), rows)
+    check(o.reshape(-1, w.d)[rows], o_ref, lse.reshape(-1)[rows], lse_ref, f"gqa {len(rows)} sampled rows")
+
+
+def test_workload_decode_every_row(fa):
+    """Llama-3.1-8B GQA decode over a 32K-key cache with the library's split count: every row."""
+    w = wl.BY_KEY["decode"]
+    n_split = fa.split_count(w.B, w.H, w.Hkv, w.T, w.Tk, w.d, w.causal)
+    say("case decode:", w.title, "splits", n_split)
+    assert n_split > 1
+    qb, kb, vb = wl.workload_inputs(w)
+    scale = np.float32(w.scale)
+    o, lse = run(fa, qb, kb, vb, w.causal, scale, n_split)
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, w.causal, float(scale))
+    check(o, o_ref, lse, lse_ref, "decode")
