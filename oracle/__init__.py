@@ -1,4 +1,4 @@
-"""CPU oracle for the exact attention forward.
+"""CPU oracle for the exact attention forward and backward.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
@@ -11,6 +11,11 @@ Contents
   is the definition the method must reproduce: ordinary softmax attention with
   the causal rule of "Flash Attention, tiled: exact attention without the T x T
   HBM matrix" (section "Ordinary causal attention").
+* ``attention_bwd_f64`` / ``attention_bwd_rows_f64``: the gradients of the same
+  attention with respect to Q, K and V for an upstream gradient dO (fp64, the
+  chain rule through the softmax one row at a time), the backward that
+  "FlashAttention and Fused Kernels: Attention Without the n x n Matrix"
+  ("Training: recompute instead of store") describes.
 * ``widen_bf16``: exact widening of bf16 bit patterns to float64, so that the
   oracle consumes the very values the GPU receives.
 * ``online`` (submodule): the online-softmax recurrence, tile by tile, used to
@@ -62,6 +67,13 @@ def _load():
         lib.fa_ref_attn_rows_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                              ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64, dp, dp]
         lib.fa_ref_attn_rows_f64.restype = ctypes.c_int
+        lib.fa_ref_attn_bwd_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                            ctypes.c_double, dp, dp, dp]
+        lib.fa_ref_attn_bwd_f64.restype = ctypes.c_int
+        ip = ctypes.POINTER(ctypes.c_int64)
+        lib.fa_ref_attn_bwd_rows_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                                 ctypes.c_double, ip, i64, dp, ip, i64, dp, dp]
+        lib.fa_ref_attn_bwd_rows_f64.restype = ctypes.c_int
         lib.fa_ref_num_threads.argtypes = []
         lib.fa_ref_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -139,6 +151,55 @@ def attention_rows_f64(q, k, v, causal: bool, scale: float, rows):
     if rc != 0:
         raise RuntimeError(f"fa_ref_attn_rows_f64 failed with code {rc}")
     return o, lse
+
+
+def attention_bwd_f64(q, k, v, do, causal: bool, scale: float):
+    """Gradients of the exact attention forward.
+
+    ``q``, ``do``: (B, Hq, Tq, d); ``k``, ``v``: (B, Hkv, Tk, d) (values or
+    bf16 bit patterns, as ``attention_f64``).  Returns ``(dq, dk, dv)`` in
+    float64 with the shapes of ``q``, ``k``, ``v``; dk and dv of a key/value
+    head sum the contributions of every query head of its group.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    _check4(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError(f"do must have the shape of q {q.shape}; got {do.shape}")
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().fa_ref_attn_bwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(do), B, Hq, Hkv, Tq, Tk, d,
+                                     int(bool(causal)), float(scale), _dptr(dq), _dptr(dk), _dptr(dv))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_attn_bwd_f64 failed with code {rc}")
+    return dq, dk, dv
+
+
+def attention_bwd_rows_f64(q, k, v, do, causal: bool, scale: float, qrows, krows):
+    """Selected gradient rows: dq for flat query rows ``(b*Hq + h)*Tq + i`` and
+    dk, dv for flat key rows ``(b*Hkv + hk)*Tk + j``.  Returns
+    ``(dq_rows, dk_rows, dv_rows)`` of shapes (len(qrows), d) and (len(krows), d)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    _check4(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError(f"do must have the shape of q {q.shape}; got {do.shape}")
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+    krows = np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.empty((qrows.shape[0], d), dtype=np.float64)
+    dk = np.empty((krows.shape[0], d), dtype=np.float64)
+    dv = np.empty((krows.shape[0], d), dtype=np.float64)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    rc = _load().fa_ref_attn_bwd_rows_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(do), B, Hq, Hkv, Tq, Tk, d,
+                                          int(bool(causal)), float(scale),
+                                          qrows.ctypes.data_as(ip), qrows.shape[0], _dptr(dq),
+                                          krows.ctypes.data_as(ip), krows.shape[0], _dptr(dk), _dptr(dv))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_attn_bwd_rows_f64 failed with code {rc}")
+    return dq, dk, dv
 
 
 def num_threads() -> int:

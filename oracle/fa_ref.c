@@ -1,5 +1,5 @@
 /*
- * fa_ref.c -- CPU oracle for the exact attention forward (fp64, plain C).
+ * fa_ref.c -- CPU oracle for the exact attention forward and backward (fp64, plain C).
  *
  * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
  * benchmark's CPU-baseline leg.  The product path never links or calls it.
@@ -162,6 +162,254 @@ int fa_ref_attn_f64(const double* q, const double* k, const double* v,
         }
         free(s);
     }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Backward.  The gradients of O = softmax(scale * Q K^T [+ causal mask]) V
+ * with respect to Q, K and V for an upstream gradient dO, written out by the
+ * chain rule one query row at a time: the step that "FlashAttention and Fused
+ * Kernels: Attention Without the n x n Matrix" ("Training: recompute instead
+ * of store") and "Flash Attention, tiled" ("More arithmetic can still be
+ * faster") describe as recomputing S and P from the inputs.  For query row i
+ * with visible keys J_i and softmax row P_i:
+ *     dP_ij = <dO_i, v_j>
+ *     D_i   = sum_{j in J_i} P_ij dP_ij          (the softmax Jacobian term)
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale * sum_j dS_ij k_j
+ *     dK_j += scale * dS_ij q_i,   dV_j += P_ij dO_i
+ * With grouped heads the contributions of every query head of a group add up
+ * in its key/value head.
+ *
+ * row_pieces: P_ij (into p) and dS_ij (into ds) of one row; returns nothing.
+ */
+static void row_pieces(const double* qi, const double* doi, const double* kh, const double* vh,
+                       int64_t n_vis, int64_t d, double scale, double* p, double* ds)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        const double* kj = kh + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += qi[c] * kj[c];
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int64_t j = 0; j < n_vis; ++j)
+        p[j] /= l;
+    double D = 0.0;
+    for (int64_t j = 0; j < n_vis; ++j) {
+        const double* vj = vh + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += doi[c] * vj[c];
+        ds[j] = dot;                       /* dP_ij for now */
+        D += p[j] * dot;
+    }
+    for (int64_t j = 0; j < n_vis; ++j)
+        ds[j] = p[j] * (ds[j] - D);
+}
+
+int fa_ref_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dout,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                        int causal, double scale,
+                        double* dq, double* dk, double* dv)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (!general_ok(B, Hq, Hkv, Tq, Tk, d, causal)) return -1;
+    const int64_t group = Hq / Hkv;
+
+    int failed = 0;
+    /* One key/value head per iteration: it alone writes its dK and dV rows,
+     * adding the rows of its query heads in a fixed order. */
+#pragma omp parallel
+    {
+        double* p = (double*)malloc((size_t)Tk * sizeof(double));
+        double* ds = (double*)malloc((size_t)Tk * sizeof(double));
+        if (!p || !ds) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bkv = 0; bkv < B * Hkv; ++bkv) {
+            if (!p || !ds) continue;
+            const int64_t b = bkv / Hkv, hk = bkv % Hkv;
+            const double* kh = k + bkv * Tk * d;
+            const double* vh = v + bkv * Tk * d;
+            double* dkh = dk + bkv * Tk * d;
+            double* dvh = dv + bkv * Tk * d;
+            for (int64_t x = 0; x < Tk * d; ++x) {
+                dkh[x] = 0.0;
+                dvh[x] = 0.0;
+            }
+            for (int64_t g = 0; g < group; ++g) {
+                const int64_t bh = b * Hq + hk * group + g;
+                for (int64_t i = 0; i < Tq; ++i) {
+                    const int64_t flat = bh * Tq + i;
+                    const double* qi = q + flat * d;
+                    const double* doi = dout + flat * d;
+                    double* dqi = dq + flat * d;
+                    const int64_t n_vis = visible_of(flat, Tq, Tk, causal);
+                    row_pieces(qi, doi, kh, vh, n_vis, d, scale, p, ds);
+                    for (int64_t c = 0; c < d; ++c)
+                        dqi[c] = 0.0;
+                    for (int64_t j = 0; j < n_vis; ++j) {
+                        const double* kj = kh + j * d;
+                        for (int64_t c = 0; c < d; ++c) {
+                            dqi[c] += scale * ds[j] * kj[c];
+                            dkh[j * d + c] += scale * ds[j] * qi[c];
+                            dvh[j * d + c] += p[j] * doi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(ds);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Selected gradient rows of the same backward: dQ for the flat query rows
+ * qrows[r] = (b*Hq + h)*Tq + i, and dK, dV for the flat key rows
+ * krows[r] = (b*Hkv + hk)*Tk + j.  A key row needs P_ij and D_i of every
+ * query row that sees it, so the row statistics (log-sum-exp and D) of the
+ * query heads of every listed key row are computed first, over all their
+ * rows.  Same formulas as fa_ref_attn_bwd_f64.
+ */
+int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, const double* dout,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                             int causal, double scale,
+                             const int64_t* qrows, int64_t n_qrows, double* dq_rows,
+                             const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows)
+{
+    if (!q || !k || !v || !dout) return -1;
+    if (!general_ok(B, Hq, Hkv, Tq, Tk, d, causal) || n_qrows < 0 || n_krows < 0) return -1;
+    if (n_qrows > 0 && (!qrows || !dq_rows)) return -1;
+    if (n_krows > 0 && (!krows || !dk_rows || !dv_rows)) return -1;
+    for (int64_t r = 0; r < n_qrows; ++r)
+        if (qrows[r] < 0 || qrows[r] >= B * Hq * Tq) return -1;
+    for (int64_t r = 0; r < n_krows; ++r)
+        if (krows[r] < 0 || krows[r] >= B * Hkv * Tk) return -1;
+    const int64_t group = Hq / Hkv;
+
+    /* Query heads whose statistics the key rows need. */
+    const int64_t n_bh = B * Hq;
+    char* need = (char*)calloc((size_t)n_bh, 1);
+    double* lse = (double*)malloc((size_t)n_bh * (size_t)Tq * sizeof(double));
+    double* D = (double*)malloc((size_t)n_bh * (size_t)Tq * sizeof(double));
+    if (!need || !lse || !D) {
+        free(need); free(lse); free(D);
+        return -2;
+    }
+    for (int64_t r = 0; r < n_krows; ++r) {
+        const int64_t bkv = krows[r] / Tk;
+        const int64_t b = bkv / Hkv, hk = bkv % Hkv;
+        for (int64_t g = 0; g < group; ++g)
+            need[b * Hq + hk * group + g] = 1;
+    }
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc((size_t)Tk * sizeof(double));
+        double* ds = (double*)malloc((size_t)Tk * sizeof(double));
+        if (!p || !ds) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* dQ rows: independent. */
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_qrows; ++r) {
+            if (!p || !ds) continue;
+            const int64_t flat = qrows[r];
+            const int64_t kvh = kv_head_of(flat, Hq, Hkv, Tq);
+            const double* kh = k + kvh * Tk * d;
+            const int64_t n_vis = visible_of(flat, Tq, Tk, causal);
+            row_pieces(q + flat * d, dout + flat * d, kh, v + kvh * Tk * d, n_vis, d, scale, p, ds);
+            double* out = dq_rows + r * d;
+            for (int64_t c = 0; c < d; ++c)
+                out[c] = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j)
+                for (int64_t c = 0; c < d; ++c)
+                    out[c] += scale * ds[j] * kh[j * d + c];
+        }
+        /* Row statistics of the needed heads: lse_i = m_i + ln l_i and D_i. */
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t flat = 0; flat < n_bh * Tq; ++flat) {
+            if (!p || !ds || !need[flat / Tq]) continue;
+            const int64_t kvh = kv_head_of(flat, Hq, Hkv, Tq);
+            const double* kh = k + kvh * Tk * d;
+            const double* vh = v + kvh * Tk * d;
+            const int64_t n_vis = visible_of(flat, Tq, Tk, causal);
+            const double* qi = q + flat * d;
+            const double* doi = dout + flat * d;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < n_vis; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += qi[c] * kh[j * d + c];
+                p[j] = scale * dot;
+                if (p[j] > m) m = p[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j)
+                l += exp(p[j] - m);
+            const double lse_i = m + log(l);
+            double Di = 0.0;
+            for (int64_t j = 0; j < n_vis; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += doi[c] * vh[j * d + c];
+                Di += exp(p[j] - lse_i) * dot;
+            }
+            lse[flat] = lse_i;
+            D[flat] = Di;
+        }
+        /* dK, dV rows: sums over the query rows that see the key. */
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_krows; ++r) {
+            const int64_t bkv = krows[r] / Tk, j = krows[r] % Tk;
+            const int64_t b = bkv / Hkv, hk = bkv % Hkv;
+            const double* kj = k + krows[r] * d;
+            const double* vj = v + krows[r] * d;
+            double* dkj = dk_rows + r * d;
+            double* dvj = dv_rows + r * d;
+            for (int64_t c = 0; c < d; ++c) {
+                dkj[c] = 0.0;
+                dvj[c] = 0.0;
+            }
+            for (int64_t g = 0; g < group; ++g) {
+                const int64_t bh = b * Hq + hk * group + g;
+                for (int64_t i = 0; i < Tq; ++i) {
+                    const int64_t flat = bh * Tq + i;
+                    if (j >= visible_of(flat, Tq, Tk, causal)) continue;
+                    const double* qi = q + flat * d;
+                    const double* doi = dout + flat * d;
+                    double s = 0.0, dp = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        s += qi[c] * kj[c];
+                        dp += doi[c] * vj[c];
+                    }
+                    const double pij = exp(scale * s - lse[flat]);
+                    const double dsij = pij * (dp - D[flat]);
+                    for (int64_t c = 0; c < d; ++c) {
+                        dkj[c] += scale * dsij * qi[c];
+                        dvj[c] += pij * doi[c];
+                    }
+                }
+            }
+        }
+        free(p);
+        free(ds);
+    }
+    free(need); free(lse); free(D);
     return failed ? -2 : 0;
 }
 

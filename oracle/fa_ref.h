@@ -1,5 +1,5 @@
 /*
- * fa_ref.h -- CPU oracle for the exact attention forward.
+ * fa_ref.h -- CPU oracle for the exact attention forward and backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
  * or call this.  It is used by the tests, by the smoke check and by the
@@ -71,6 +71,25 @@ int fa_ref_attn_rows_f64(const double* q, const double* k, const double* v,
                          int causal, double scale,
                          const int64_t* rows, int64_t n_rows,
                          double* o_rows, double* lse_rows);
+
+/* Backward of the general problem for upstream gradient dout ([B][Hq][Tq][d]):
+ * dq is [B][Hq][Tq][d], dk and dv are [B][Hkv][Tk][d] (each the sum over the
+ * query heads of its group).  With P the softmax rows, dP = dout V^T,
+ * D_i = sum_j P_ij dP_ij and dS = P * (dP - D): dq = scale dS K,
+ * dk = scale dS^T Q, dv = P^T dout.  Same return codes as above. */
+int fa_ref_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dout,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                        int causal, double scale,
+                        double* dq, double* dk, double* dv);
+
+/* Selected rows of the backward: dq for flat query rows qrows[r] =
+ * (b*Hq + h)*Tq + i into dq_rows [n_qrows][d]; dk, dv for flat key rows
+ * krows[r] = (b*Hkv + hk)*Tk + j into dk_rows, dv_rows [n_krows][d]. */
+int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, const double* dout,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                             int causal, double scale,
+                             const int64_t* qrows, int64_t n_qrows, double* dq_rows,
+                             const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows);
 
 /* Number of OpenMP threads the oracle runs with. */
 int fa_ref_num_threads(void);
