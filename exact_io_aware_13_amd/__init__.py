@@ -1,11 +1,13 @@
-"""Exact attention forward for MI355X (gfx950): hand-written HIP kernels behind a C ABI.
+"""Exact attention forward and backward for MI355X (gfx950): hand-written HIP kernels behind a C ABI.
 
 ``fwd(q, k, v, causal, scale=None, n_split=1) -> (o, lse)`` and ``fwd_out``
 call the ``fa_fwd`` / ``fa_fwd_gqa`` / ``fa_fwd_split`` entry points of
-``libfa.so`` (declared in ``include/fa.h``).  The library is loaded on first
-use; a missing build raises instead of falling back.
+``libfa.so`` (declared in ``include/fa.h``); ``bwd(q, k, v, o, lse, do, causal,
+scale=None) -> (dq, dk, dv)`` and ``bwd_out`` call ``fa_bwd``.  The library is
+loaded on first use; a missing build raises instead of falling back.
 """
-from ._lib import (FAError, fwd, fwd_out, load, split_count, split_workspace_bytes,  # noqa: F401
-                   status_string)
+from ._lib import (FAError, bwd, bwd_out, bwd_workspace_bytes, fwd, fwd_out, load,  # noqa: F401
+                   split_count, split_workspace_bytes, status_string)
 
-__all__ = ["fwd", "fwd_out", "load", "status_string", "split_count", "split_workspace_bytes", "FAError"]
+__all__ = ["fwd", "fwd_out", "bwd", "bwd_out", "bwd_workspace_bytes", "load", "status_string", "split_count",
+           "split_workspace_bytes", "FAError"]

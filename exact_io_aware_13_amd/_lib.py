@@ -1,7 +1,7 @@
 """ctypes binding of ``libfa.so`` (the C ABI in ``include/fa.h``).
 
-Argument marshalling only: every step of the attention forward runs in the
-HIP kernels.  torch supplies device memory and the current HIP stream.  If the
+Argument marshalling only: every step of the attention forward and backward
+runs in the HIP kernels.  torch supplies device memory and the current HIP stream.  If the
 library has not been built, loading fails loudly; there is no fallback.
 """
 from __future__ import annotations
@@ -25,14 +25,15 @@ FA_ERR_HIP = 7
 FA_ERR_ARG = 8
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
-            "fa_status_string", "fa_hip_error_string")
+            "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string",
+            "fa_bwd_hip_error_string")
 
 _lib = None
 
 
 class FAError(RuntimeError):
-    def __init__(self, status: int, message: str):
-        super().__init__(f"fa_fwd failed with status {status}: {message}")
+    def __init__(self, status: int, message: str, entry: str = "fa_fwd"):
+        super().__init__(f"{entry} failed with status {status}: {message}")
         self.status = status
 
 
@@ -56,6 +57,13 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
         lib.fa_fwd_split_count.restype = ctypes.c_int64
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                               ctypes.c_float, vp, ctypes.c_size_t, vp]
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd_hip_error_string.argtypes = []
+        lib.fa_bwd_hip_error_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_hip_error_string.argtypes = []
@@ -98,12 +106,25 @@ def split_count(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: boo
     return int(load().fa_fwd_split_count(B, Hq, Hkv, Tq, Tk, d, int(bool(causal))))
 
 
-def _check(status: int) -> None:
+def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int, dq_ptr: int,
+               dk_ptr: int, dv_ptr: int, B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: int,
+               scale: float, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """Call ``fa_bwd`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, B, Hq, Hkv, Tq,
+                             Tk, d, int(causal), float(scale), ws_ptr, ws_bytes, stream))
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Tq: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, Hq, Tq))
+
+
+def _check(status: int, entry: str = "fa_fwd") -> None:
     if status != FA_OK:
         msg = status_string(status)
         if status == FA_ERR_HIP:
-            msg += f" ({load().fa_hip_error_string().decode()})"
-        raise FAError(status, msg)
+            err = load().fa_bwd_hip_error_string() if entry == "fa_bwd" else load().fa_hip_error_string()
+            msg += f" ({err.decode()})"
+        raise FAError(status, msg, entry)
 
 
 def _check_tensors(q, k, v):
@@ -187,3 +208,44 @@ def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None =
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     fwd_out(q, k, v, o, lse, causal, scale, n_split)
     return o, lse
+
+
+def bwd_out(q, k, v, o, lse, do, dq, dk, dv, causal: bool, scale: float | None = None, workspace=None) -> None:
+    """Gradients of the forward into caller buffers ``dq`` (like q), ``dk``, ``dv`` (like k, v).
+
+    ``o`` and ``lse`` are the forward's outputs for the same q, k, v, causal
+    and scale; ``do`` is the upstream gradient of o (bf16, shaped like q).
+    ``workspace`` is a uint8 GPU tensor of at least ``bwd_workspace_bytes``
+    bytes; if it is not given, one is allocated here.
+    """
+    import torch
+    _check_tensors(q, k, v)
+    B, Hq, Tq, d = q.shape
+    for name, t, like in (("o", o, q), ("do", do, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if (not isinstance(t, torch.Tensor) or t.shape != like.shape or t.dtype != torch.bfloat16
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped {tuple(like.shape)} on q's device")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Tq) on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, Hq, Tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, k.shape[1], Tq, k.shape[2], d,
+                        int(bool(causal)), float(scale), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), stream)
+        _check(st, "fa_bwd")
+
+
+def bwd(q, k, v, o, lse, do, causal: bool, scale: float | None = None):
+    """Gradients of the exact attention forward; returns ``(dq, dk, dv)`` (bf16)."""
+    import torch
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    bwd_out(q, k, v, o, lse, do, dq, dk, dv, causal, scale)
+    return dq, dk, dv

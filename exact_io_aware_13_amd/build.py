@@ -1,6 +1,7 @@
 """Build the gfx950 HIP library ``libfa.so`` in-tree with hipcc.
 
-The library exports the C ABI declared in ``include/fa.h``.  Flags: gfx950
+The library (forward and backward sources) exports the C ABI declared in
+``include/fa.h``.  Flags: gfx950
 only, -O3, packed-fp32 instructions disabled in the device pass
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass prints a
 harmless notice that it does not know that feature), and ``-fno-honor-nans``:
@@ -15,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
@@ -37,11 +38,12 @@ def compile_flags():
 
 
 def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = True) -> str:
-    """Compile ``csrc/fa_fwd.hip`` into ``libfa.so``; returns the library path."""
+    """Compile ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip`` into ``libfa.so``; returns the library path."""
     out = out or LIB
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+    newest = max(os.path.getmtime(p) for p in SRCS + [os.path.join(INCLUDE, "fa.h")])
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= newest:
         return out
-    cmd = [hipcc()] + compile_flags() + list(extra or []) + ["-shared", "-o", out + ".tmp", SRC]
+    cmd = [hipcc()] + compile_flags() + list(extra or []) + ["-shared", "-o", out + ".tmp"] + SRCS
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

@@ -1,7 +1,7 @@
 /*
- * fa.h -- C ABI of the exact attention forward for MI355X (gfx950).
+ * fa.h -- C ABI of the exact attention forward and backward for MI355X (gfx950).
  *
- * One operation, the exact attention forward of one or more heads:
+ * The exact attention forward of one or more heads:
  *
  *   O[b,h,i,:] = sum_{j visible to i} softmax_j(scale * q_i . k_j) * v_j
  *   lse[b,h,i] = ln sum_{j visible to i} exp(scale * q_i . k_j)
@@ -18,6 +18,7 @@
  * "FlashAttention and Fused Kernels: Attention Without the n x n Matrix",
  * Step 4, returned in natural-log units, so that P_ij = exp(s_ij - lse_i).
  *
+ * fa_bwd is its training backward (the gradients with respect to q, k, v).
  * All entry points are plain C: pointers, sizes and a HIP stream handle.
  */
 #ifndef FA_H
@@ -141,11 +142,54 @@ size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t T
  * valid. */
 int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal);
 
+/*
+ * fa_bwd -- gradients of the exact attention forward, enqueued on `stream`.
+ *
+ * The backward that keeps only O and the per-row log-sum-exp from the forward
+ * and recomputes the score and probability tiles from q and k ("FlashAttention
+ * and Fused Kernels: Attention Without the n x n Matrix", "Training: recompute
+ * instead of store").  With P_ij = exp(scale * q_i . k_j - lse_i) over the
+ * visible keys, dP = dO V^T, D_i = dO_i . O_i and dS = P * (dP - D):
+ *     dq = scale * dS K,   dk = scale * dS^T Q,   dv = P^T dO,
+ * where dk and dv of a key/value head add up every query head of its group.
+ *
+ * q, o, dout, dq : bf16 [B][Hq][Tq][d];  k, v, dk, dv : bf16 [B][Hkv][Tk][d];
+ *           dense row-major, 16-byte aligned.  o and lse are what the forward
+ *           (fa_fwd, fa_fwd_gqa or fa_fwd_split) returned for these q, k, v,
+ *           causal and scale; dout is the upstream gradient of o.
+ * lse     : fp32 [B][Hq][Tq], natural-log units, 4-byte aligned, finite.
+ * dq, dk, dv : written (bf16, round-to-nearest-even from fp32 sums); they must
+ *           not overlap each other, any input or the workspace.
+ * B, Hq, Hkv, Tq, Tk, d, causal, scale : as fa_fwd_split (head mapping, causal
+ *           rule for the last Tq positions, Tq <= Tk when causal).
+ * workspace, workspace_bytes : device scratch owned by the caller, 16-byte
+ *           aligned, at least fa_bwd_workspace_bytes(B, Hq, Tq) bytes; it
+ *           holds D and lse * log2(e) per row and is overwritten.  Calls that
+ *           share it must not run concurrently.
+ *
+ * Three kernels are enqueued in order: the per-row D, then dk and dv, then
+ * dq.  No atomics are used: equal inputs give bit-equal gradients.
+ * Errors as fa_fwd_split; FA_ERR_NULL if any pointer (workspace included) is
+ * NULL, FA_ERR_ARG for a workspace that is too small or overlapping buffers.
+ * A failed launch's text is in fa_bwd_hip_error_string().
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                 int causal, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fa_bwd needs: 8 per query row (0 for invalid sizes). */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status status);
 
-/* Text of the last HIP error seen by fa_fwd on the calling thread, or "" */
+/* Text of the last HIP error seen by the forward entry points on the calling
+ * thread, or "" */
 const char* fa_hip_error_string(void);
+
+/* Text of the last HIP error seen by fa_bwd on the calling thread, or "" */
+const char* fa_bwd_hip_error_string(void);
 
 #ifdef __cplusplus
 }

@@ -174,3 +174,33 @@ def test_split_count_advice(lib):
     # grouped decode folds the group into rows: fewer workgroups, so more splits
     assert _lib.split_count(8, 32, 8, 1, 32768, 128, True) > _lib.split_count(8, 32, 32, 1, 32768, 128, True)
     assert _lib.split_count(1, 32, 33, 1, 4096, 128, True) == 1       # invalid grouping
+
+
+# fa_bwd: the same validation before any HIP call.
+def bcall(q=A, k=2 * A, v=3 * A, o=4 * A, do=5 * A, lse=6 * A, dq=7 * A, dk=8 * A, dv=9 * A, B=1, Hq=1, Hkv=1,
+          Tq=16, Tk=16, d=64, causal=1, scale=0.125, ws=10 * A, ws_bytes=1 << 12):
+    return _lib.fa_bwd_raw(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale, ws, ws_bytes, 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"])
+def test_bwd_null_pointer(lib, which):
+    assert bcall(**{which: 0}) == _lib.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _lib.FA_ERR_SHAPE), (dict(Tq=0), _lib.FA_ERR_SHAPE), (dict(Hq=3, Hkv=2), _lib.FA_ERR_SHAPE),
+    (dict(Tq=17, Tk=16), _lib.FA_ERR_SHAPE), (dict(d=96), _lib.FA_ERR_HEAD_DIM),
+    (dict(scale=math.nan), _lib.FA_ERR_SCALE), (dict(causal=2), _lib.FA_ERR_ARG),
+    (dict(dq=7 * A + 8), _lib.FA_ERR_ALIGN), (dict(lse=6 * A + 2), _lib.FA_ERR_ALIGN),
+    (dict(ws_bytes=16 * 8 - 1), _lib.FA_ERR_ARG), (dict(dk=2 * A), _lib.FA_ERR_ARG),
+    (dict(dq=7 * A, dv=7 * A + 16), _lib.FA_ERR_ARG), (dict(ws=A + 64), _lib.FA_ERR_ARG),
+    (dict(Tq=1 << 31, Tk=1 << 31), _lib.FA_ERR_OVERFLOW),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bcall(**kw) == code
+
+
+def test_bwd_workspace_bytes(lib):
+    assert _lib.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
+    assert _lib.bwd_workspace_bytes(0, 3, 5) == 0
+    assert lib.fa_bwd_hip_error_string() == b""

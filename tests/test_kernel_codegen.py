@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def asm(tmp_path_factory):
     out = tmp_path_factory.mktemp("isa") / "fa_fwd.s"
     cmd = [build.hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + \
-        ["--cuda-device-only", "-S", "-o", str(out), build.SRC]
+        ["--cuda-device-only", "-S", "-o", str(out), build.SRCS[0]]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
 
