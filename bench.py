@@ -7,7 +7,12 @@ causal), a roofline object for the kernel (measured with HIP events on the
 launch stream) and a CPU-baseline object (the fp64 oracle timed on a bounded
 row sample on the host cores).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--pass fwd|bwd]
+
+``--pass bwd`` times the backward instead (one step = one ``fa_bwd`` call: the
+per-row D pass, the dK/dV kernel and the dQ kernel), with O and lse from the
+forward computed before the timed region; its FLOP count is the usual 2.5x the
+forward's (five T x T x d products instead of two).
 """
 from __future__ import annotations
 
@@ -95,6 +100,111 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float):
     }
 
 
+def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, dob, target_s: float):
+    """The backward oracle as it stands, on the first heads of the workload (whole rows).
+
+    The oracle parallelises over key/value heads, so the sample takes as many
+    key/value heads as it has threads (all of them if that covers the
+    workload), and is repeated until about ``target_s`` seconds have passed."""
+    import oracle
+    oracle.build(force=False)
+    g = w.H // w.Hkv
+    n_kv = max(1, min(w.Hkv, oracle.num_threads()))
+    sub = lambda x, n: x[:1, :n]
+    qs, dos = sub(qb, n_kv * g), sub(dob, n_kv * g)
+    ks, vs = sub(kb, n_kv), sub(vb, n_kv)
+    per_row_vis = (np.arange(w.T) + (w.Tk - w.T) + 1) if w.causal else np.full(w.T, w.Tk)
+    flops = 2.5 * 4.0 * w.d * float(per_row_vis.sum()) * n_kv * g
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention_bwd_f64(qs, ks, vs, dos, w.causal, float(np.float32(w.scale)))
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 8:
+            break
+    whole = n_kv == w.Hkv and w.B == 1
+    return {
+        "value": passes * flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ((f"the whole workload ({w.B * w.H} heads)" if whole else
+                    f"{n_kv * g} of {w.B * w.H} query heads ({n_kv} key/value heads), every row")
+                   + f", {passes} pass(es) ({passes * flops / 1e9:.1f} GFLOP at 2.5x the forward's count "
+                     f"in {dt:.1f} s, fp64, OpenMP over key/value heads)"),
+    }
+
+
+def bench_bwd(args, w: wl.Workload, dev) -> int:
+    """Time K backward steps; print one JSON line."""
+    import torch
+    import exact_io_aware_13_amd as fa
+
+    qb, kb, vb = wl.workload_inputs(w)
+    dob = wl.workload_grad_output(w)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v, do = up(qb), up(kb), up(vb), up(dob)
+    scale = float(np.float32(w.scale))
+    o, lse = fa.fwd(q, k, v, w.causal, scale, n_split=1)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    workspace = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.T), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.bwd_out(q, k, v, o, lse, do, dq, dk, dv, w.causal, scale, workspace=workspace)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps   # one fa_bwd call: D pass + dK/dV + dQ kernels
+    ms_per_step = wall_ms / args.steps
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all().item(), "non-finite gradient"
+
+    flops = 2.5 * w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    config = {"workload": w.title + " (backward)", "B": w.B, "H": w.H, "T": w.T, "d": w.d, "causal": w.causal}
+    if w.Hkv != w.H:
+        config["Hkv"] = w.Hkv
+    config["pct_of_bf16_peak"] = round(100.0 * value / PEAK_BF16_TFLOPS, 2)
+    out = {
+        "metric": f"attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak, {w.title}",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; dO a separate draw)",
+        "config": config,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 4),
+                     "kernels": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel (one fa_bwd call)"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_bwd(w, qb, kb, vb, dob, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +215,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=wl.BENCH_KEY, choices=sorted(wl.BY_KEY))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one device copy of this size (counter calibration runs)")
     args = ap.parse_args(argv)
@@ -122,6 +234,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.load()
+    if args.pass_ == "bwd":
+        return bench_bwd(args, w, dev)
 
     qb, kb, vb = wl.workload_inputs(w)
 

@@ -15,16 +15,20 @@
 // the gradients are bit-reproducible.
 //   * prep: D_i = dO_i . O_i (fp32 from the bf16 O the forward wrote) and
 //     lse_i * log2(e), one pass over O and dO into the workspace.
-//   * dK/dV kernel, key-major: a workgroup of 4 waves owns 128 keys of one
-//     key/value head, each wave 32 of them, with its K and V rows held in
-//     registers as MFMA operands for the whole kernel.  It walks the query
-//     tiles (64 rows, every query head of the group) that see its keys,
-//     copying Q, dO, lse and D tiles HBM -> LDS (buffer_load ... lds, double
-//     buffered).  Per tile a wave computes S = Q K^T and dP = dO V^T with the
-//     keys on the lanes (v_mfma_f32_32x32x16_bf16; each lane holds 32 query
-//     rows of ONE key), so the bf16 P and dS accumulators are directly the B
-//     operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are
-//     transposed LDS reads (ds_read_b64_tr_b16) of the same dO and Q tiles.
+//   * dK/dV kernel, key-major: a workgroup of 8 waves owns 128 keys of one
+//     key/value head.  The two waves of a SIMD take the same 32 keys and split
+//     the work: one holds K and computes S = Q K^T, P and dV^T += dO^T P, the
+//     other holds V and computes dP = dO V^T, dS = P (dP - D) and
+//     dK^T += Q^T dS, with P passed through LDS.  It walks the 32-row query
+//     tiles (every query head of the group) that see its keys, copying Q, dO,
+//     lse and D tiles HBM -> LDS (buffer_load ... lds, a ring of four slots).
+//     S and dP are computed with the keys on the lanes
+//     (v_mfma_f32_32x32x16_bf16; each lane holds 32 query rows of ONE key), so
+//     the bf16 P and dS accumulators are directly the B operands of the dV and
+//     dK products, whose A operands are transposed LDS reads
+//     (ds_read_b64_tr_b16) of the same dO and Q tiles.  The two waves of a
+//     SIMD are phase-shifted by software pipelining, so that one's
+//     exponentials overlap the other's matrix products.
 //   * dQ kernel, query-major: the forward's shape.  A workgroup of 4 waves
 //     owns 128 query rows, each lane one row, with Q and dO held in registers;
 //     it streams 64-key K and V tiles through LDS, computes S^T = K Q^T and
@@ -206,29 +210,36 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const uint16_t* __rest
 
 // ---------------------------------------------------------------------------
 // dK/dV kernel.  A workgroup of 8 waves owns 128 keys.  Waves w and w + 4
-// share SIMD w % 4 and the same 32 keys: wave w (the "P wave") computes
-// S = Q K^T, P and dV^T += dO^T P; wave w + 4 (the "dS wave") computes
-// dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS, taking P from LDS.  Each
-// wave thus holds one of K, V and one of dK, dV (about 150 registers), two
-// waves fit a SIMD, and one wave's exponentials run while the other's matrix
-// products do.  Query tiles of 32 rows; per tile two barriers:
-//   phase A:  P wave: S, P (written to LDS), bf16 P;   dS wave: dP;
-//   phase B:  P wave: dV^T += dO^T P;                  dS wave: dS, dK^T += Q^T dS.
-// LDS: two tile slots (Q, dO, lse2, D), fetched one tile ahead, and the P
-// exchange area (4 KB per wave pair).
-constexpr int kQRows = 32;   // query rows per dK/dV tile
+// share SIMD w % 4 and the same 32 keys: wave w (the "P wave") holds K and
+// computes S = Q K^T, P and dV^T += dO^T P; wave w + 4 (the "dS wave") holds
+// V and computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS, taking P
+// from LDS.  Each wave holds one of K, V and one of dK, dV (about 150
+// registers), so two waves fit a SIMD.  Query tiles of 32 rows; each tile is
+// two phases, and in each phase one wave of a SIMD does VALU work while the
+// other keeps the matrix unit busy:
+//   phase A(i):  P wave:  P(i) from S(i) (to LDS and to bf16)
+//                dS wave: dP(i) = dO_i V^T, then dK^T += Q_{i-1}^T dS(i-1)
+//   phase B(i):  P wave:  dV^T += dO_i^T P(i), then S(i+1) = Q_{i+1} K^T
+//                dS wave: dS(i) = P(i) (dP(i) - D)
+// LDS: a ring of tile slots (Q, dO, lse2, D) and the P exchange area (4 KB
+// per wave pair and 32-row block).  A tile is in use from phase B of the tile
+// before it to phase A of the tile after it; it is fetched into the slot of
+// the tile before that as soon as that one is done, at least a tile ahead.
+// 32-row tiles: 64-row tiles (three slots) measured the same at d = 128 and
+// slower at d = 64.
+constexpr int kQRows = 32;                     // query rows per dK/dV tile
+constexpr int kRB = kQRows / 32;               // 32-row blocks per tile
+constexpr int kRing = kQRows == 32 ? 4 : 3;    // tile slots
 template <int D>
 struct KvLds {
     static constexpr int kTile = kQRows * 2 * D;
-    static constexpr int kSlot = 2 * kTile + 512;
-    static constexpr int kQ(int k) { return k * kSlot; }
-    static constexpr int kDo(int k) { return k * kSlot + kTile; }
-    static constexpr int kLse(int k) { return k * kSlot + 2 * kTile; }
-    static constexpr int kD(int k) { return k * kSlot + 2 * kTile + 256; }
-    static constexpr int kX = 2 * kSlot;                 // P exchange: [pair][4][64 lanes][16 bytes]
-    static constexpr int kBytes = kX + 4 * 4096;
-    static constexpr int kBlocks = kTile / 1024;          // 1 KB blocks per tile of one tensor
-    static constexpr int kLoads = 2 * kBlocks / 8;        // 1 KB buffer->LDS copies per wave per tile (Q, then dO)
+    static constexpr int kSlot = 2 * kTile;                 // Q tile, then dO tile
+    static constexpr int kStats = kRing * kSlot;            // per slot: 64 lse2, then 64 D (one copy each)
+    static constexpr int kPad = kStats + kRing * 512;       // 6 waves x 256 B of dummy copies
+    static constexpr int kX = kPad + 6 * 256;               // P exchange: [pair][row block][4][64 lanes][16 B]
+    static constexpr int kBytes = kX + 4 * 4096 * kRB;
+    static constexpr int kBlocks = kTile / 1024;            // 1 KB blocks per tile of one tensor
+    static constexpr int kLoads = 2 * kBlocks / 8;          // 1 KB copies per wave per tile (Q, then dO)
 };
 
 template <int D, bool CAUSAL>
@@ -281,7 +292,10 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* __restrict__ Q, const
     const int t_mask = CAUSAL ? max(0, (k0 + 31 - off + kQRows - 1) / kQRows - qt0) : 0;
 
     // Buffer->LDS copies: the Q tile's and then the dO tile's 1 KB blocks are
-    // dealt to the 8 waves; this lane copies one 16-byte chunk of each.
+    // dealt to the 8 waves; this lane copies one 16-byte chunk of each.  Each
+    // wave issues kLoads + 1 copies per tile (waves 0, 1: lse2, D; the others
+    // a dummy), so that a tile's copies are one fixed count in every wave.
+    constexpr int kPerTile = L::kLoads + 1;
     uint32_t goff[L::kLoads];
     int gdst[L::kLoads];
     bool gdo[L::kLoads];
@@ -293,10 +307,11 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* __restrict__ Q, const
         const int qd = jb * 64 + lane;
         const int r = qd / G::kChunks, p = qd % G::kChunks;
         goff[c] = r * G::kRowBytes + 16 * (p ^ swz<D>(r));
-        gdst[c] = (gdo[c] ? L::kTile : 0) + jb * 1024;
+        gdst[c] = jb * 1024;
     }
-    auto load = [&] __device__ (int it, auto slot) {
-        constexpr int k = decltype(slot)::value;
+    auto slot_of = [&] __device__ (int it) { return kRing == 4 ? (it & 3) : it % kRing; };
+    auto load = [&] __device__ (int it) {
+        const int k = slot_of(it);
         const int h = hk * a.group + it / per_head;
         const int q0 = (qt0 + it % per_head) * kQRows;
         const size_t row0 = ((size_t)b * a.hq + h) * (size_t)Tq + q0;
@@ -305,13 +320,13 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* __restrict__ Q, const
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(DO + row0 * D, bytes);
 #pragma unroll
         for (int c = 0; c < L::kLoads; ++c)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(gdo[c] ? rd : rq, (FB_LDS void*)(lds + L::kQ(k) + gdst[c]), 16,
-                                                     goff[c], 0, 0, 0);
-        if (wave < 2) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave == 0 ? LSE2 : DD) + row0, (uint32_t)(Tq - q0) * 4u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FB_LDS void*)(lds + (wave == 0 ? L::kLse(k) : L::kD(k))), 4,
-                                                     (uint32_t)lane * 4u, 0, 0, 0);
-        }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(gdo[c] ? rd : rq,
+                                                     (FB_LDS void*)(lds + k * L::kSlot + (gdo[c] ? L::kTile : 0) + gdst[c]),
+                                                     16, goff[c], 0, 0, 0);
+        // lse2 (wave 0) and D (wave 1) of the tile's rows; 64 values per copy.
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave == 1 ? DD : LSE2) + row0, (uint32_t)(Tq - q0) * 4u);
+        const int dst = wave == 0 ? L::kStats + k * 512 : wave == 1 ? L::kStats + k * 512 + 256 : L::kPad + 256 * (wave - 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FB_LDS void*)(lds + dst), 4, (uint32_t)lane * 4u, 0, 0, 0);
     };
 
     const TileOffsets<D> to(lane);
@@ -321,89 +336,147 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* __restrict__ Q, const
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
     const float c = a.c;
-    FB_LDS char* const xp = lds + L::kX + pair * 4096 + lane * 16;   // this lane's P exchange slots
+    FB_LDS char* const xp = lds + L::kX + pair * 4096 * kRB + lane * 16;   // this lane's P exchange slots
 
     // S = Q K^T (P wave) or dP = dO V^T (dS wave) of the tile in slot k.
-    auto product = [&] __device__ (auto slot) {
-        constexpr int k = decltype(slot)::value;
-        f32x16 r;
+    auto product = [&] __device__ (int k, f32x16 (&r)[kRB]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = 0.0f;
-        FB_LDS const char* const src = lds + (pwave ? L::kQ(k) : L::kDo(k));
+        for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int st = 0; st < G::kDSteps; ++st)
-            r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(src, to, 0, st), bf[st], r, 0, 0, 0);
-        return r;
+            for (int i = 0; i < 16; ++i) r[rb][i] = 0.0f;
+        FB_LDS const char* const src = lds + k * L::kSlot + (pwave ? 0 : L::kTile);
+        constexpr int N = G::kDSteps * kRB;
+        bf16x8 op[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) op[i] = row_operand<D>(src, to, i % kRB, i / kRB);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            r[i % kRB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], bf[i / kRB], r[i % kRB], 0, 0, 0);
+        // Keep kAhead operand reads in flight ahead of the MFMA that uses them.
+        constexpr int kAhead = 3 < N ? 3 : N;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < N - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     };
-    // acc += A^T B over the tile's 32 query rows (2 steps of 16): A = dO (P
-    // wave) or Q (dS wave) read transposed, B = the bf16 weights.
-    auto accumulate = [&] __device__ (auto slot, const uint32_t (&wb)[8]) {
-        constexpr int k = decltype(slot)::value;
-        FB_LDS const char* const src = lds + (pwave ? L::kDo(k) : L::kQ(k));
+    // acc += A^T B over a tile's query rows (steps of 16): A = dO (P wave) or
+    // Q (dS wave) of slot k read transposed, B = the bf16 weights.
+    auto accumulate = [&] __device__ (int k, const uint32_t (&wb)[8 * kRB]) {
+        FB_LDS const char* const src = lds + k * L::kSlot + (pwave ? L::kTile : 0);
+        constexpr int N = 2 * kRB * G::kDBlocks;
+        bf16x8 op[N];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int i = 0; i < N; ++i) op[i] = tr_operand<D>(src, to, i / G::kDBlocks, i % G::kDBlocks);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int ks = i / G::kDBlocks, db = i % G::kDBlocks;
             const bf16x8 bb = as_bf16x8(wb[4 * ks], wb[4 * ks + 1], wb[4 * ks + 2], wb[4 * ks + 3]);
-#pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(src, to, ks, db), bb, acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], bb, acc[db], 0, 0, 0);
         }
+        // Each operand is two transposed reads; keep kAhead operands in flight.
+        constexpr int kAhead = 3 < N ? 3 : N;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < N - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     };
 
-    // One tile in slot K.  Element i of a 32 x 32 tile is query row
-    // q0 + 8 (i / 4) + 4 half + i % 4 of key `key`.
-    auto tile = [&] __device__ (int it, auto slot) {
-        constexpr int K = decltype(slot)::value;
-        using Next = std::integral_constant<int, K ^ 1>;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile it has landed
-        __syncthreads();                      // ... for every wave, and tile it - 1 and the exchange area are free
-        if (it + 1 < n_it) load(it + 1, Next{});
-        const int t = it % per_head;
-        const int q0 = (qt0 + t) * kQRows;
-        const f32x16 r = product(slot);
-        uint32_t wb[8];
-        if (pwave) {
-            // P = exp2(s c - lse2), masked past each row's causal limit.
-            float p[16];
-            const int vis0 = q0 + off + 4 * half - key;   // element visible iff vis0 + 8 g + t >= 0
+    // Each role runs its own loop over the tiles; both loops pass the same
+    // barriers in the same order (two per tile).  Element i of 32-row block rb
+    // is query row q0 + 32 rb + 8 (i / 4) + 4 half + i % 4 of key `key`.
+    auto phase_b_start = [&] __device__ (int it) {
+        // Tile it + 1 has landed (with four slots, tile it + 2 may still be in flight).
+        if (kRing == 4 && it + 2 < n_it) __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);   // vmcnt(kPerTile)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                                          // vmcnt(0)
+        __syncthreads();
+        if (it + kRing - 1 < n_it) load(it + kRing - 1);   // into tile it - 1's slot
+    };
+
+    // The last slot's Q tile is read (with zero weights) by the dS waves'
+    // first, empty dK step before any tile lands there: clear it, so that the
+    // product is exactly zero.
+#pragma unroll
+    for (int z0 = 0; z0 < L::kTile; z0 += 8 * 1024)
+        if (z0 + wave * 1024 < L::kTile) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *(FB_LDS u32x4*)(lds + (kRing - 1) * L::kSlot + z0 + wave * 1024 + lane * 16) = z;
+        }
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j)
+        if (j < n_it) load(j);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (pwave) {
+        // Phase A: P (to LDS and bf16); phase B: dV^T += dO^T P, then the next
+        // tile's S (after the last tile: a dummy on stale LDS data, never used).
+        f32x16 s_next[kRB];
+        product(0, s_next);
+        for (int it = 0; it < n_it; ++it) {
+            const int k = slot_of(it);
+            const int t = it % per_head;
+            const int q0 = (qt0 + t) * kQRows;
+            __syncthreads();
             const bool masked = CAUSAL && t < t_mask;
+            FB_LDS const char* const lse_t = lds + L::kStats + k * 512;
+            uint32_t pb[8 * kRB];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *(FB_LDS const f32x4*)(lds + L::kLse(K) + 4 * (8 * g + 4 * half));
+            for (int rb = 0; rb < kRB; ++rb) {
+                const int vis0 = q0 + 32 * rb + off + 4 * half - key;   // element visible iff vis0 + 8 g + e >= 0
+                float p[16];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + e], c, -l4[e]));
-                    p[4 * g + e] = masked && vis0 < -(8 * g + e) ? 0.0f : pv;
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 l4 = *(FB_LDS const f32x4*)(lse_t + 4 * (32 * rb + 8 * g + 4 * half));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_next[rb][4 * g + e], c, -l4[e]));
+                        p[4 * g + e] = masked && vis0 < -(8 * g + e) ? 0.0f : pv;
+                    }
+                    const f32x4 pw = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                    *(FB_LDS f32x4*)(xp + rb * 4096 + g * 1024) = pw;
                 }
-                const f32x4 pw = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
-                *(FB_LDS f32x4*)(xp + g * 1024) = pw;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) pb[8 * rb + n] = pack_bf16x2(p[2 * n], p[2 * n + 1]);
             }
-#pragma unroll
-            for (int n = 0; n < 8; ++n) wb[n] = pack_bf16x2(p[2 * n], p[2 * n + 1]);
+            phase_b_start(it);
+            accumulate(k, pb);
+            product(slot_of(it + 1), s_next);
         }
-        __syncthreads();   // P of this tile is in LDS
-        if (!pwave) {
-            // dS = P (dP - D).
-            float ds[16];
+    } else {
+        // Phase A: dP, then dK^T += Q^T dS of the previous tile; phase B:
+        // dS = P (dP - D).
+        uint32_t ds_prev[8 * kRB];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 p4 = *(FB_LDS const f32x4*)(xp + g * 1024);
-                const f32x4 d4 = *(FB_LDS const f32x4*)(lds + L::kD(K) + 4 * (8 * g + 4 * half));
+        for (int n = 0; n < 8 * kRB; ++n) ds_prev[n] = 0u;
+        for (int it = 0; it < n_it; ++it) {
+            const int k = slot_of(it);
+            __syncthreads();
+            f32x16 dp[kRB];
+            product(k, dp);
+            accumulate(slot_of(it + kRing - 1), ds_prev);   // first tile: zero weights on a zeroed tile
+            phase_b_start(it);
+            FB_LDS const char* const d_t = lds + L::kStats + k * 512 + 256;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (r[4 * g + e] - d4[e]);
+            for (int rb = 0; rb < kRB; ++rb) {
+                float ds[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 p4 = *(FB_LDS const f32x4*)(xp + rb * 4096 + g * 1024);
+                    const f32x4 d4 = *(FB_LDS const f32x4*)(d_t + 4 * (32 * rb + 8 * g + 4 * half));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (dp[rb][4 * g + e] - d4[e]);
+                }
+#pragma unroll
+                for (int n = 0; n < 8; ++n) ds_prev[8 * rb + n] = pack_bf16x2(ds[2 * n], ds[2 * n + 1]);
             }
-#pragma unroll
-            for (int n = 0; n < 8; ++n) wb[n] = pack_bf16x2(ds[2 * n], ds[2 * n + 1]);
         }
-        accumulate(slot, wb);
-    };
-
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    if (n_it > 0) load(0, S0{});
-    for (int it = 0; it < n_it; it += 2) {
-        tile(it, S0{});
-        if (it + 1 >= n_it) break;
-        tile(it + 1, S1{});
+        // The last tile's dK^T += Q^T dS (its Q tile is still in place).
+        if (n_it > 0) accumulate(slot_of(n_it - 1), ds_prev);
     }
 
     // dV = dV^T (P wave), dK = scale * dK^T (dS wave), bf16; rows past Tk dropped by the descriptor.

@@ -155,6 +155,12 @@ def workload_inputs(w: Workload):
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
+def workload_grad_output(w: Workload) -> np.ndarray:
+    """The bf16 bits of the upstream gradient dO (shape of Q) for a backward run."""
+    rng = np.random.default_rng(w.seed + 7919)
+    return f32_to_bf16_bits(rng.standard_normal(size=w.shape, dtype=np.float32))
+
+
 def spike_masks(shape, seed: int):
     """The (q_mask, k_mask) row masks ``draw_f32`` applies for spiky workloads."""
     rng = np.random.default_rng(seed)

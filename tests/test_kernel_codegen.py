@@ -52,3 +52,41 @@ def test_lds_reads_do_not_wait_on_tile_loads(asm):
         waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
                  if a.startswith("s_waitcnt") and "vmcnt" in a and b.startswith("ds_read")]
         assert not waits, (name, [body[i:i + 2] for i in waits[:3]])
+
+
+@pytest.fixture(scope="module")
+def asm_bwd(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "fa_bwd.s"
+    cmd = [build.hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + \
+        ["--cuda-device-only", "-S", "-o", str(out), build.SRCS[1]]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _bwd_kernels(asm):
+    for m in re.finditer(r"^(_ZN\S*fa_bwd_\w+_kernel\S*):", asm, re.M):
+        start = m.end()
+        end = asm.index(".Lfunc_end", start)
+        body = [l.strip() for l in asm[start:end].splitlines()]
+        yield m.group(1), [l for l in body if l and not l.startswith((";", "."))]
+
+
+def test_every_backward_variant_is_compiled(asm_bwd):
+    names = [n for n, _ in _bwd_kernels(asm_bwd)]
+    assert sum("prep" in n for n in names) == 2, names      # d
+    assert sum("dkdv" in n for n in names) == 4, names      # d x causal
+    assert sum("dq_kernel" in n for n in names) == 4, names
+
+
+def test_backward_has_no_register_spills_and_fits_two_waves_per_simd(asm_bwd):
+    spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm_bwd)]
+    assert spills and max(spills) == 0
+    counts = [int(x) for x in re.findall(r"\.vgpr_count:\s+(\d+)", asm_bwd)]
+    assert max(counts) <= 256, counts
+
+
+def test_backward_lds_reads_do_not_wait_on_tile_loads(asm_bwd):
+    for name, body in _bwd_kernels(asm_bwd):
+        waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
+                 if a.startswith("s_waitcnt") and "vmcnt" in a and "lgkmcnt" not in a and b.startswith("ds_read")]
+        assert not waits, (name, [body[i:i + 2] for i in waits[:3]])
