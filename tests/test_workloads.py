@@ -55,3 +55,13 @@ def test_workload_table():
     assert (c4.B, c4.H, c4.T, c4.d, c4.causal) == (1, 32, 8192, 128, True)
     assert abs(c4.flops() - 549.755813888e9) < 1e3
     assert c4.algorithmic_bytes() == 8 * 32 * 8192 * 128 + 4 * 32 * 8192
+
+
+def test_grad_output_draw_is_seeded_and_separate():
+    w = wl.BY_KEY["c1"]
+    a, b = wl.workload_grad_output(w), wl.workload_grad_output(w)
+    assert a.dtype == np.uint16 and a.shape == w.shape and np.array_equal(a, b)
+    q, _, _ = wl.workload_inputs(w)
+    assert not np.array_equal(a, q)
+    x = wl.bf16_bits_to_f32(a)
+    assert abs(float(x.mean())) < 0.1 and 0.9 < float(x.std()) < 1.1
