@@ -37,21 +37,36 @@ KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic_causal_b1h32t8192d128.json")
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+BWD_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_bwd.hip")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_traffic_causal_b1h32t8192d128.json")
+
+
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(key: str):
-    """HBM bytes per launch from the committed counter runs, if they match this kernel source."""
+def measured_traffic(key: str, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
+    """HBM bytes per launch (per call) from the committed counter runs, if they match this kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != key:
+    if t.get("kernel_sha256_16") != kernel_hash(src) or t.get("workload") != key:
         return None
     return t.get("bytes_per_launch")
+
+
+def copy_probe(mib: int, dev) -> None:
+    """One device-to-device copy of `mib` MiB, whose counters calibrate FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float):
@@ -135,6 +150,13 @@ def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, dob, target_s: float):
     }
 
 
+def bwd_algorithmic_bytes(w: wl.Workload) -> int:
+    """Q, K, V, O, dO and lse read once; dQ, dK, dV written once (the D workspace is not counted)."""
+    q = w.B * w.H * w.T * w.d * 2
+    kv = w.B * w.Hkv * w.Tk * w.d * 2
+    return 4 * q + 4 * kv + w.B * w.H * w.T * 4
+
+
 def bench_bwd(args, w: wl.Workload, dev) -> int:
     """Time K backward steps; print one JSON line."""
     import torch
@@ -155,6 +177,8 @@ def bench_bwd(args, w: wl.Workload, dev) -> int:
     def step():
         fa.bwd_out(q, k, v, o, lse, do, dq, dk, dv, w.causal, scale, workspace=workspace)
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         step()
@@ -195,8 +219,9 @@ def bench_bwd(args, w: wl.Workload, dev) -> int:
         "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; dO a separate draw)",
         "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel_ms": round(kernel_ms, 4),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.key, BWD_TRAFFIC_FILE, BWD_SRC),
+                     "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": bwd_algorithmic_bytes(w),
                      "kernels": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel (one fa_bwd call)"},
     }
     if not args.no_cpu_baseline:
@@ -254,12 +279,7 @@ def main(argv=None) -> int:
         fa.fwd_out(q, k, v, o, lse, w.causal, scale, n_split=n_split, workspace=workspace)
 
     if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(args.copy_probe_mib, dev)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):

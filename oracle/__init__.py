@@ -74,6 +74,9 @@ def _load():
         lib.fa_ref_attn_bwd_rows_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                                  ctypes.c_double, ip, i64, dp, ip, i64, dp, dp]
         lib.fa_ref_attn_bwd_rows_f64.restype = ctypes.c_int
+        lib.fa_ref_attn_bwd_rows_given_d_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                                         ctypes.c_double, dp, ip, i64, dp, ip, i64, dp, dp]
+        lib.fa_ref_attn_bwd_rows_given_d_f64.restype = ctypes.c_int
         lib.fa_ref_num_threads.argtypes = []
         lib.fa_ref_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -177,10 +180,14 @@ def attention_bwd_f64(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv
 
 
-def attention_bwd_rows_f64(q, k, v, do, causal: bool, scale: float, qrows, krows):
+def attention_bwd_rows_f64(q, k, v, do, causal: bool, scale: float, qrows, krows, d_rows=None):
     """Selected gradient rows: dq for flat query rows ``(b*Hq + h)*Tq + i`` and
     dk, dv for flat key rows ``(b*Hkv + hk)*Tk + j``.  Returns
-    ``(dq_rows, dk_rows, dv_rows)`` of shapes (len(qrows), d) and (len(krows), d)."""
+    ``(dq_rows, dk_rows, dv_rows)`` of shapes (len(qrows), d) and (len(krows), d).
+
+    ``d_rows`` (optional, float64 of shape (B, Hq, Tq)) replaces the softmax
+    Jacobian term D_i = sum_j P_ij dP_ij of every row; only the rows that the
+    requested gradients depend on are read."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     _check4(q, k, v)
     if do.shape != q.shape:
@@ -193,10 +200,17 @@ def attention_bwd_rows_f64(q, k, v, do, causal: bool, scale: float, qrows, krows
     dk = np.empty((krows.shape[0], d), dtype=np.float64)
     dv = np.empty((krows.shape[0], d), dtype=np.float64)
     ip = ctypes.POINTER(ctypes.c_int64)
-    rc = _load().fa_ref_attn_bwd_rows_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(do), B, Hq, Hkv, Tq, Tk, d,
-                                          int(bool(causal)), float(scale),
-                                          qrows.ctypes.data_as(ip), qrows.shape[0], _dptr(dq),
-                                          krows.ctypes.data_as(ip), krows.shape[0], _dptr(dk), _dptr(dv))
+    if d_rows is None:
+        dptr = ctypes.cast(None, ctypes.POINTER(ctypes.c_double))
+    else:
+        d_rows = np.ascontiguousarray(d_rows, dtype=np.float64)
+        if d_rows.shape != (B, Hq, Tq):
+            raise ValueError(f"d_rows must have shape {(B, Hq, Tq)}; got {d_rows.shape}")
+        dptr = _dptr(d_rows)
+    rc = _load().fa_ref_attn_bwd_rows_given_d_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(do), B, Hq, Hkv, Tq, Tk, d,
+                                                  int(bool(causal)), float(scale), dptr,
+                                                  qrows.ctypes.data_as(ip), qrows.shape[0], _dptr(dq),
+                                                  krows.ctypes.data_as(ip), krows.shape[0], _dptr(dk), _dptr(dv))
     if rc != 0:
         raise RuntimeError(f"fa_ref_attn_bwd_rows_f64 failed with code {rc}")
     return dq, dk, dv

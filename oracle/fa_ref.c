@@ -289,6 +289,23 @@ int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, 
                              const int64_t* qrows, int64_t n_qrows, double* dq_rows,
                              const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows)
 {
+    return fa_ref_attn_bwd_rows_given_d_f64(q, k, v, dout, B, Hq, Hkv, Tq, Tk, d, causal, scale, NULL,
+                                            qrows, n_qrows, dq_rows, krows, n_krows, dk_rows, dv_rows);
+}
+
+/*
+ * The same with the softmax Jacobian term D_i taken from `d_rows` (one value
+ * per flat query row, [B][Hq][Tq]) instead of computed as sum_j P_ij dP_ij;
+ * NULL means computed.  With D_i = dO_i . O_i for the exact O this is the same
+ * result (D_i = dO_i . O_i is an identity); it lets a test measure what a
+ * rounded O in that product alone changes.
+ */
+int fa_ref_attn_bwd_rows_given_d_f64(const double* q, const double* k, const double* v, const double* dout,
+                                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                                     int causal, double scale, const double* d_rows,
+                                     const int64_t* qrows, int64_t n_qrows, double* dq_rows,
+                                     const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows)
+{
     if (!q || !k || !v || !dout) return -1;
     if (!general_ok(B, Hq, Hkv, Tq, Tk, d, causal) || n_qrows < 0 || n_krows < 0) return -1;
     if (n_qrows > 0 && (!qrows || !dq_rows)) return -1;
@@ -333,6 +350,15 @@ int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, 
             const double* kh = k + kvh * Tk * d;
             const int64_t n_vis = visible_of(flat, Tq, Tk, causal);
             row_pieces(q + flat * d, dout + flat * d, kh, v + kvh * Tk * d, n_vis, d, scale, p, ds);
+            if (d_rows) {
+                /* ds holds P (dP - D) for the computed D; rebuild it with the given one. */
+                for (int64_t j = 0; j < n_vis; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        dot += dout[flat * d + c] * v[kvh * Tk * d + j * d + c];
+                    ds[j] = p[j] * (dot - d_rows[flat]);
+                }
+            }
             double* out = dq_rows + r * d;
             for (int64_t c = 0; c < d; ++c)
                 out[c] = 0.0;
@@ -370,7 +396,7 @@ int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, 
                 Di += exp(p[j] - lse_i) * dot;
             }
             lse[flat] = lse_i;
-            D[flat] = Di;
+            D[flat] = d_rows ? d_rows[flat] : Di;
         }
         /* dK, dV rows: sums over the query rows that see the key. */
 #pragma omp for schedule(dynamic, 4)

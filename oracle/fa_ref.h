@@ -91,6 +91,15 @@ int fa_ref_attn_bwd_rows_f64(const double* q, const double* k, const double* v, 
                              const int64_t* qrows, int64_t n_qrows, double* dq_rows,
                              const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows);
 
+/* fa_ref_attn_bwd_rows_f64 with the softmax Jacobian term D_i of every flat
+ * query row given in d_rows ([B][Hq][Tq]) instead of computed; NULL means
+ * computed, exactly as fa_ref_attn_bwd_rows_f64. */
+int fa_ref_attn_bwd_rows_given_d_f64(const double* q, const double* k, const double* v, const double* dout,
+                                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                                     int causal, double scale, const double* d_rows,
+                                     const int64_t* qrows, int64_t n_qrows, double* dq_rows,
+                                     const int64_t* krows, int64_t n_krows, double* dk_rows, double* dv_rows);
+
 /* Number of OpenMP threads the oracle runs with. */
 int fa_ref_num_threads(void);
 

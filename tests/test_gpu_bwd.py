@@ -200,3 +200,48 @@ def test_bwd_full_size_sampled(fa, B, Hq, Hkv, T, d, causal, heads):
     check("dq", dq.reshape(-1, d_)[qrows], rq, label)
     check("dk", dk.reshape(-1, d_)[krows], rk, label)
     check("dv", dv.reshape(-1, d_)[krows], rv, label)
+
+
+def test_bwd_long_context_spiky_sampled(fa):
+    """The long-context spiky workload (B=1 H=32 T=32768 d=128, 1% of Q and K rows x8): dq rows
+    and dk / dv rows of one head, including spiked query rows and the first and last positions.
+
+    Spiked rows give nearly one-hot softmax rows, where dP - D cancels and the
+    bf16 rounding of O in D = dO . O (the only O the backward receives)
+    dominates dS.  The bound therefore adds twice that rounding's own effect,
+    computed by the oracle alone: the gradients with D_i = dO_i . bf16(O_i),
+    O from the oracle forward, against the exact ones."""
+    w = wl.BY_KEY["c5"]
+    label = "bwd sampled " + w.title
+    say("case", label)
+    qb, kb, vb = wl.workload_inputs(w)
+    dob = wl.workload_grad_output(w)
+    scale = np.float32(w.scale)
+    dq, dk, dv = gpu_grads(fa, qb, kb, vb, dob, True, scale)
+    q_mask, k_mask = wl.spike_masks(w.shape, w.seed)
+    h = 17
+    rng = np.random.default_rng(5)
+    pos = set(int(x) for x in rng.choice(w.T, 20, replace=False)) | {0, 1, 63, 64, w.T - 1}
+    pos |= set(int(x) for x in np.flatnonzero(q_mask[0, h])[:6]) | set(int(x) for x in np.flatnonzero(k_mask[0, h])[:6])
+    rows = sorted(h * w.T + p for p in pos)
+    ref = oracle.attention_bwd_rows_f64(qb, kb, vb, dob, True, float(scale), rows, rows)
+    # D from the bf16-rounded oracle O of head h (every row of the head: dK, dV rows need them all)
+    head_rows = np.arange(h * w.T, (h + 1) * w.T)
+    o_h, _ = oracle.attention_rows_f64(qb, kb, vb, True, float(scale), head_rows)
+    o_h16 = oracle.widen_bf16(wl.f32_to_bf16_bits(o_h.astype(np.float32)))
+    d_rows = np.zeros((w.B, w.H, w.T))
+    d_rows[0, h] = np.einsum("id,id->i", oracle.widen_bf16(dob[0, h]), o_h16)
+    ref_d = oracle.attention_bwd_rows_f64(qb, kb, vb, dob, True, float(scale), rows, rows, d_rows=d_rows)
+    d_ = w.d
+    for name, got, r, rd in (("dq", dq.reshape(-1, d_)[rows], ref[0], ref_d[0]),
+                             ("dk", dk.reshape(-1, d_)[rows], ref[1], ref_d[1]),
+                             ("dv", dv.reshape(-1, d_)[rows], ref[2], ref_d[2])):
+        R = max(1.0, float(np.abs(r).max()))
+        e_max = float(np.abs(rd - r).max())
+        e_rel = float(np.linalg.norm(rd - r) / max(np.linalg.norm(r), 1e-30))
+        max_abs = float(np.abs(got - r).max())
+        rel = float(np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30))
+        say(f"[{label}] {name}: max-abs {max_abs:.3e} (R {R:.2f}) rel-L2 {rel:.3e}; "
+            f"bf16-O-in-D effect max-abs {e_max:.3e} rel-L2 {e_rel:.3e}")
+        assert np.all(np.isfinite(got)), name
+        assert max_abs <= MAX_ABS_REL * R + 2 * e_max and rel <= REL_L2 + 2 * e_rel, (name, max_abs, rel)

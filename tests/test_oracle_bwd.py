@@ -49,3 +49,22 @@ def test_bwd_rejects_bad_sizes():
         oracle.attention_bwd_rows_f64(q, k, k, q, False, 1.0, [8], [])
     with pytest.raises(RuntimeError):
         oracle.attention_bwd_rows_f64(q, k, k, q, False, 1.0, [], [-1])
+
+
+def test_bwd_rows_given_d_is_the_identity_for_exact_o():
+    """D_i = dO_i . O_i (O from the oracle forward) given explicitly reproduces the computed D."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, Tq, Tk, d = 1, 4, 2, 11, 11, 6
+    q, do = rng.standard_normal((B, Hq, Tq, d)), rng.standard_normal((B, Hq, Tq, d))
+    k, v = rng.standard_normal((B, Hkv, Tk, d)) * 2, rng.standard_normal((B, Hkv, Tk, d))
+    o, _ = oracle.attention_f64(q, k, v, True, 0.6)
+    D = np.einsum("bhid,bhid->bhi", do, o)
+    qr, kr = np.arange(B * Hq * Tq), np.arange(B * Hkv * Tk)
+    a = oracle.attention_bwd_rows_f64(q, k, v, do, True, 0.6, qr, kr)
+    b = oracle.attention_bwd_rows_f64(q, k, v, do, True, 0.6, qr, kr, d_rows=D)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() <= 1e-12
+    # and a perturbed D moves the gradients (the override is read)
+    c = oracle.attention_bwd_rows_f64(q, k, v, do, True, 0.6, qr, kr, d_rows=D + 0.01)
+    assert np.abs(c[0] - a[0]).max() > 1e-4 and np.abs(c[1] - a[1]).max() > 1e-4
+    assert np.abs(c[2] - a[2]).max() <= 1e-12   # dV does not involve D
