@@ -25,8 +25,7 @@ FA_ERR_HIP = 7
 FA_ERR_ARG = 8
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
-            "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string",
-            "fa_bwd_hip_error_string")
+            "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
 
 _lib = None
 
@@ -62,8 +61,6 @@ def load() -> ctypes.CDLL:
         lib.fa_bwd.restype = ctypes.c_int
         lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        lib.fa_bwd_hip_error_string.argtypes = []
-        lib.fa_bwd_hip_error_string.restype = ctypes.c_char_p
         lib.fa_status_string.argtypes = [ctypes.c_int]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_hip_error_string.argtypes = []
@@ -122,8 +119,7 @@ def _check(status: int, entry: str = "fa_fwd") -> None:
     if status != FA_OK:
         msg = status_string(status)
         if status == FA_ERR_HIP:
-            err = load().fa_bwd_hip_error_string() if entry == "fa_bwd" else load().fa_hip_error_string()
-            msg += f" ({err.decode()})"
+            msg += f" ({load().fa_hip_error_string().decode()})"
         raise FAError(status, msg, entry)
 
 

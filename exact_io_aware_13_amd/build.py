@@ -40,7 +40,8 @@ def compile_flags():
 def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = True) -> str:
     """Compile ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip`` into ``libfa.so``; returns the library path."""
     out = out or LIB
-    newest = max(os.path.getmtime(p) for p in SRCS + [os.path.join(INCLUDE, "fa.h")])
+    newest = max(os.path.getmtime(p) for p in SRCS + [os.path.join(INCLUDE, "fa.h"),
+                                                      os.path.join(PKG, "csrc", "fa_internal.h")])
     if not force and os.path.exists(out) and os.path.getmtime(out) >= newest:
         return out
     cmd = [hipcc()] + compile_flags() + list(extra or []) + ["-shared", "-o", out + ".tmp"] + SRCS

@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_internal.h"
 
 namespace {
 
@@ -671,8 +672,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dq_block<D, CAUSAL>(a.q, a.k, a.v, a.dout, a.lse2, a.dd, a.dq, a, (FB_LDS char*)smem);
 }
 
-thread_local char g_bwd_hip_error[256] = "";
-
 bool overlaps(const void* x, size_t nx, const void* y, size_t ny) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
     return a < b + ny && b < a + nx;
@@ -770,11 +769,10 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
         d == 128 ? launch_bwd<128>(a, causal != 0, rows, o16, lse, lse2, dd, n_kv_wg, n_q_wg, stream)
                  : launch_bwd<64>(a, causal != 0, rows, o16, lse, lse2, dd, n_kv_wg, n_q_wg, stream);
     if (err != hipSuccess) {
-        std::snprintf(g_bwd_hip_error, sizeof(g_bwd_hip_error), "%s: %s", hipGetErrorName(err),
-                      hipGetErrorString(err));
+        fa_internal::record_hip_error(err);
         return FA_ERR_HIP;
     }
-    g_bwd_hip_error[0] = '\0';
+    fa_internal::clear_hip_error();
     return FA_OK;
 }
 
@@ -793,5 +791,3 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale, workspace,
                    workspace_bytes, stream);
 }
-
-extern "C" const char* fa_bwd_hip_error_string(void) { return g_bwd_hip_error; }

@@ -67,6 +67,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_internal.h"
 
 namespace {
 
@@ -593,8 +594,6 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const float* __restrict
     if (t == 0) lse[row] = m + kLn2 * __builtin_amdgcn_logf(l);
 }
 
-thread_local char g_hip_error[256] = "";
-
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + nb && y < x + na;
@@ -724,14 +723,26 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
         }
     }
     if (err != hipSuccess) {
-        std::snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(err), hipGetErrorString(err));
+        fa_internal::record_hip_error(err);
         return FA_ERR_HIP;
     }
-    g_hip_error[0] = '\0';
+    fa_internal::clear_hip_error();
     return FA_OK;
 }
 
 }  // namespace
+
+namespace fa_internal {
+
+thread_local char g_hip_error[256] = "";
+
+void record_hip_error(hipError_t err) {
+    std::snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(err), hipGetErrorString(err));
+}
+
+void clear_hip_error() { g_hip_error[0] = '\0'; }
+
+}  // namespace fa_internal
 
 extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                             int64_t H, int64_t T, int64_t d, int causal, float scale, hipStream_t stream) {
@@ -795,4 +806,4 @@ extern "C" const char* fa_status_string(fa_status status) {
     return "unknown status";
 }
 
-extern "C" const char* fa_hip_error_string(void) { return g_hip_error; }
+extern "C" const char* fa_hip_error_string(void) { return fa_internal::g_hip_error; }

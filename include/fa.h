@@ -171,7 +171,6 @@ int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
  * dq.  No atomics are used: equal inputs give bit-equal gradients.
  * Errors as fa_fwd_split; FA_ERR_NULL if any pointer (workspace included) is
  * NULL, FA_ERR_ARG for a workspace that is too small or overlapping buffers.
- * A failed launch's text is in fa_bwd_hip_error_string().
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv,
@@ -184,12 +183,9 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq);
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(fa_status status);
 
-/* Text of the last HIP error seen by the forward entry points on the calling
- * thread, or "" */
+/* Text of the HIP error of the calling thread's last call of any entry point
+ * above, or "" when that call launched successfully */
 const char* fa_hip_error_string(void);
-
-/* Text of the last HIP error seen by fa_bwd on the calling thread, or "" */
-const char* fa_bwd_hip_error_string(void);
 
 #ifdef __cplusplus
 }

@@ -203,4 +203,11 @@ def test_bwd_rejects(lib, kw, code):
 def test_bwd_workspace_bytes(lib):
     assert _lib.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
     assert _lib.bwd_workspace_bytes(0, 3, 5) == 0
-    assert lib.fa_bwd_hip_error_string() == b""
+    assert lib.fa_hip_error_string() == b""
+
+
+def test_library_exports_nothing_undeclared(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == _declared_functions(), exported ^ _declared_functions()
