@@ -16,7 +16,9 @@ Recipe: ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float32
 standard normals of shape (B, H, T, d).  For the spiky long-context workload it
 then draws a Q-row mask and a K-row mask, each Bernoulli(0.01) per (b, h, t),
 and multiplies the selected rows by 8 (a power of two, so exact in bf16).  The
-values are then rounded to bf16 with round-to-nearest-even.
+values are then rounded to bf16 with round-to-nearest-even.  For the FP8
+workloads the same float32 draw is divided by a per-tensor descale factor
+(amax / 448) and rounded to OCP FP8 E4M3, ties to even.
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ class Workload:
     hkv: int = 0                 # key/value heads (0: one per query head)
     tk: int = 0                  # keys (0: T, the square problem)
     n_split: int = 1             # key splits for the split forward (None: the library's advice)
+    fp8: bool = False            # inputs in FP8 E4M3 with per-tensor descale factors
 
     @property
     def scale(self) -> float:
@@ -75,10 +78,12 @@ class Workload:
         return 4.0 * self.B * self.H * pairs * self.d
 
     def algorithmic_bytes(self) -> int:
-        """One read of Q, K, V and one write of O (2 B/element) plus lse (4 B/row)."""
+        """One read of Q, K, V (2 B/element, 1 B in FP8) and one write of O
+        (2 B/element) plus lse (4 B/row)."""
         nq = self.B * self.H * self.T
         nkv = self.B * self.Hkv * self.Tk
-        return 2 * nq * self.d * 2 + 2 * nkv * self.d * 2 + 4 * nq
+        eb = 1 if self.fp8 else 2
+        return nq * self.d * (eb + 2) + 2 * nkv * self.d * eb + 4 * nq
 
 
 WORKLOADS = [
@@ -96,6 +101,9 @@ WORKLOADS = [
              seed=6, sampled_rows=True, hkv=8),
     Workload("decode", "Llama-3.1-8B GQA decode B=8 Hq=32 Hkv=8 Tq=1 Tk=32768 d=128, split keys", 8, 32, 1, 128,
              True, seed=7, hkv=8, tk=32768, n_split=None),
+    # The c4 shape and draw with FP8 E4M3 inputs (per-tensor descale factors).
+    Workload("c4fp8", "Llama-3.1-8B-shaped causal prefill B=1 H=32 T=8192 d=128, FP8 E4M3 inputs", 1, 32, 8192,
+             128, True, seed=4, sampled_rows=True, fp8=True),
 ]
 BY_KEY = {w.key: w for w in WORKLOADS}
 
@@ -153,6 +161,57 @@ def workload_inputs(w: Workload):
     k = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
     v = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to OCP FP8 E4M3 (round to nearest, ties to even), saturating
+    at +-448; returns uint8 bits (sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent field 0 holds the subnormals m * 2^-9)."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input values")
+    a = np.abs(x)
+    # binade exponent, at least -6 (the subnormals share the spacing of [2^-6, 2^-5))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = np.exp2(e - 3.0)
+    r = np.minimum(np.rint(a / step) * step, E4M3_MAX)   # np.rint rounds ties to even
+    # re-derive the fields of the rounded value (rounding may carry into the next binade)
+    e2 = np.floor(np.log2(np.maximum(r, 2.0 ** -6)))
+    sub = r < 2.0 ** -6
+    m_sub = np.rint(r / 2.0 ** -9)
+    m_nrm = np.rint(r / np.exp2(e2) * 8.0) - 8.0
+    bits = np.where(sub, m_sub, (e2 + 7.0) * 8.0 + m_nrm).astype(np.uint8)
+    return bits | np.where(np.signbit(x) & (r > 0), np.uint8(0x80), np.uint8(0))
+
+
+def e4m3_descale(x: np.ndarray) -> np.float32:
+    """Per-tensor descale factor amax / 448 (fp32; 1 for an all-zero tensor)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    return np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """(bits, descale) with x ~= descale * e4m3(bits): x / descale rounded to E4M3."""
+    ds = e4m3_descale(x)
+    return f32_to_e4m3_bits(np.asarray(x, dtype=np.float64) / np.float64(ds)), ds
+
+
+def workload_inputs_fp8(w: Workload):
+    """FP8 E4M3 Q, K, V of a workload: the same float32 draw as the bf16 inputs,
+    each tensor divided by its descale factor and rounded to E4M3.  Returns
+    ``(q8, k8, v8, (q_descale, k_descale, v_descale))``."""
+    if w.kv_shape == w.shape:
+        q, k, v = draw_f32(w.shape, w.seed, w.spikes)
+    else:
+        rng = np.random.default_rng(w.seed)
+        q = rng.standard_normal(size=w.shape, dtype=np.float32)
+        k = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
+        v = rng.standard_normal(size=w.kv_shape, dtype=np.float32)
+    (q8, qd), (k8, kd), (v8, vd) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    return q8, k8, v8, (qd, kd, vd)
 
 
 def workload_grad_output(w: Workload) -> np.ndarray:
