@@ -9,7 +9,8 @@ row sample on the host cores).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--pass fwd|bwd]
 
-``--pass bwd`` times the backward instead (one step = one ``fa_bwd`` call: the
+``--workload c4fp8`` times the FP8 forward (``fa_fwd_fp8``) on the same shape
+with E4M3 inputs, against the fp8 MFMA peak.  ``--pass bwd`` times the backward instead (one step = one ``fa_bwd`` call: the
 per-row D pass, the dK/dV kernel and the dQ kernel), with O and lse from the
 forward computed before the timed region; its FLOP count is the usual 2.5x the
 forward's (five T x T x d products instead of two).
@@ -32,11 +33,14 @@ sys.path.insert(0, ROOT)
 from exact_io_aware_13_amd import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic_causal_b1h32t8192d128.json")
 
 
+FP8_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_fwd_fp8.hip")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_traffic_causal_b1h32t8192d128.json")
 BWD_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_bwd.hip")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_traffic_causal_b1h32t8192d128.json")
 
@@ -69,8 +73,9 @@ def copy_probe(mib: int, dev) -> None:
     del src, dst
 
 
-def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float):
-    """The oracle as it stands, on an evenly spaced row sample sized to ~target_s seconds."""
+def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float, widened=None):
+    """The oracle as it stands, on an evenly spaced row sample sized to ~target_s seconds.
+    ``widened``: the float64 operands the oracle reads, when they are not bf16 bits."""
     import oracle
     oracle.build(force=False)
     n_rows_total = w.B * w.H * w.T
@@ -84,7 +89,7 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float):
         return np.unique(np.linspace(0, n_rows_total - 1, n).astype(np.int64))
 
     # widen only what the oracle reads: all heads' rows are needed for K/V
-    qd, kd, vd = (oracle.widen_bf16(x) for x in (qb, kb, vb))
+    qd, kd, vd = widened if widened is not None else (oracle.widen_bf16(x) for x in (qb, kb, vb))
     probe = sample(64)
     t0 = time.perf_counter()
     oracle.attention_rows_f64(qd, kd, vd, w.causal, float(np.float32(w.scale)), probe)
@@ -230,6 +235,72 @@ def bench_bwd(args, w: wl.Workload, dev) -> int:
     return 0
 
 
+def bench_fp8(args, w: wl.Workload, dev) -> int:
+    """The FP8 forward (``fa_fwd_fp8``) on an FP8 workload; one step = one launch."""
+    import torch
+    import exact_io_aware_13_amd as fa
+    q8, k8, v8, ds = wl.workload_inputs_fp8(w)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+    o = torch.empty(w.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    scale = float(np.float32(w.scale))
+    descales = tuple(float(x) for x in ds)
+
+    def step():
+        fa.fwd_fp8_out(q, k, v, o, lse, w.causal, scale, descales)
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall_ms / args.steps
+    assert torch.isfinite(lse).all().item(), "non-finite lse"
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": measured_traffic(w.key, FP8_TRAFFIC_FILE, FP8_SRC),
+            "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": w.algorithmic_bytes()}
+    config = {"workload": w.title, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "causal": w.causal,
+              "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+              "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)}
+    out = {
+        "metric": f"attention fwd TFLOP/s and % of fp8 MFMA peak, {w.title}",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded i.i.d. N(0,1), per-tensor scaled to FP8 E4M3)",
+        "config": config,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import fp8 as ofp8
+        widened = tuple(ofp8.dequantize(x, d) for x, d in zip((q8, k8, v8), ds))
+        out["cpu_baseline"] = cpu_baseline(w, q8, k8, v8, args.cpu_seconds, widened=widened)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +332,8 @@ def main(argv=None) -> int:
     fa.load()
     if args.pass_ == "bwd":
         return bench_bwd(args, w, dev)
+    if w.fp8:
+        return bench_fp8(args, w, dev)
 
     qb, kb, vb = wl.workload_inputs(w)
 

@@ -25,7 +25,7 @@ FA_ERR_HIP = 7
 FA_ERR_ARG = 8
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
-            "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
+            "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
         lib.fa_fwd_split_count.restype = ctypes.c_int64
+        f32 = ctypes.c_float
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, f32, f32, f32,
+                                   f32, vp]
+        lib.fa_fwd_fp8.restype = ctypes.c_int
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                ctypes.c_float, vp, ctypes.c_size_t, vp]
         lib.fa_bwd.restype = ctypes.c_int
@@ -101,6 +105,14 @@ def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: in
 
 def split_count(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: bool) -> int:
     return int(load().fa_fwd_split_count(B, Hq, Hkv, Tq, Tk, d, int(bool(causal))))
+
+
+def fa_fwd_fp8_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
+                   Tq: int, Tk: int, d: int, causal: int, scale: float, q_descale: float, k_descale: float,
+                   v_descale: float, stream: int) -> int:
+    """Call ``fa_fwd_fp8`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
+                                 float(scale), float(q_descale), float(k_descale), float(v_descale), stream))
 
 
 def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int, dq_ptr: int,
@@ -203,6 +215,63 @@ def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None =
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     fwd_out(q, k, v, o, lse, causal, scale, n_split)
+    return o, lse
+
+
+def _check_fp8_tensors(q, k, v):
+    import torch
+    fp8 = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in fp8:
+            raise ValueError(f"{name} must hold E4M3 bytes (uint8 or float8_e4m3fn), got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous (B, H, T, d) tensor, got {tuple(t.shape)}")
+    if k.shape != v.shape:
+        raise ValueError(f"k, v shapes differ: {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q {tuple(q.shape)} and k/v {tuple(k.shape)} differ in batch or head size")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def fwd_fp8_out(q, k, v, o, lse, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0)) -> None:
+    """FP8 forward into caller buffers ``o`` (bf16, shaped like q) and ``lse`` (fp32, (B, Hq, Tq)).
+
+    ``q``: (B, Hq, Tq, d), ``k, v``: (B, Hkv, Tk, d), E4M3 bytes (uint8 or
+    float8_e4m3fn); ``descales`` = (q_descale, k_descale, v_descale), the
+    operands being ``descale * e4m3``.  Calls ``fa_fwd_fp8``.
+    """
+    import torch
+    _check_fp8_tensors(q, k, v)
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q on q's device")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Tq) on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = (float(x) for x in descales)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_fp8_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                            Tq, Tk, d, int(bool(causal)), float(scale), qd, kd, vd, stream)
+        _check(st, "fa_fwd_fp8")
+
+
+def fwd_fp8(q, k, v, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0)):
+    """FP8 E4M3 attention forward; returns ``(o, lse)`` with ``o`` bf16 and
+    ``lse`` float32 (B, Hq, Tq).  Arguments as ``fwd_fp8_out``."""
+    import torch
+    _check_fp8_tensors(q, k, v)
+    B, Hq, Tq, d = q.shape
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    fwd_fp8_out(q, k, v, o, lse, causal, scale, descales)
     return o, lse
 
 

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library ``libfa.so`` in-tree with hipcc.
 
-The library (forward and backward sources) exports the C ABI declared in
+The library (the bf16 forward, the backward and the FP8 forward) exports the C ABI declared in
 ``include/fa.h``.  Flags: gfx950
 only, -O3, packed-fp32 instructions disabled in the device pass
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass prints a
@@ -16,7 +16,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_bwd.hip"),
+        os.path.join(PKG, "csrc", "fa_fwd_fp8.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
@@ -38,7 +39,7 @@ def compile_flags():
 
 
 def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = True) -> str:
-    """Compile ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip`` into ``libfa.so``; returns the library path."""
+    """Compile the ``csrc/*.hip`` sources of ``SRCS`` into ``libfa.so``; returns the library path."""
     out = out or LIB
     newest = max(os.path.getmtime(p) for p in SRCS + [os.path.join(INCLUDE, "fa.h"),
                                                       os.path.join(PKG, "csrc", "fa_internal.h")])

@@ -143,6 +143,50 @@ size_t fa_fwd_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t T
 int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal);
 
 /*
+ * fa_fwd_fp8 -- the forward with FP8 E4M3 inputs, enqueued on `stream`.
+ *
+ * The FP8 mode named for FlashAttention-3 ("FlashAttention and Fused Kernels:
+ * Attention Without the n x n Matrix", "Four generations"; the pages give no
+ * recipe).  The operands are descale * e4m3: q, k, v hold OCP FP8 E4M3 bytes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; the patterns
+ * 0x7F / 0xFF are NaN and must not occur) with one fp32 descale factor per
+ * tensor, and the result is the attention of those values:
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * qd * kd * q_i . k_j) * vd * v_j
+ *
+ * with the head mapping and causal rule of fa_fwd_split (no key split).  Both
+ * products run on the FP8 matrix cores; the probability weights enter the PV
+ * product rounded to E4M3 (round to nearest even), the only approximation
+ * beyond rounding order.  The weights are 2^3 * exp2 of the score against a
+ * lazily moved reference that never exceeds the row max; they lie in
+ * (0, 448] and the largest is at least 8.  O is normalised by the sum of the
+ * rounded weights, so each output element is within
+ *   sum_j max(2^-4 w_j, min(2^-13 / Z, w_j)) |vd v_j - O| (to first order)
+ * of the exact value, w the exact weights and Z = sum_j exp(s_j - max s),
+ * plus the matrix cores' summation of each 64-product block (measured within
+ * 2^-10.9 of the largest product), fp32 accumulation and the bf16 store.
+ * lse uses fp32 weights.
+ *
+ * q       : device pointer, E4M3 bytes [B][Hq][Tq][d], 16-byte aligned.
+ * k, v    : device pointers, E4M3 bytes [B][Hkv][Tk][d], 16-byte aligned.
+ * o       : device pointer, bf16 [B][Hq][Tq][d], 16-byte aligned.
+ * lse     : device pointer, fp32 [B][Hq][Tq], natural log, 4-byte aligned.
+ * B, Hq, Hkv, Tq, Tk, d, causal, scale : as fa_fwd_split.
+ * q_descale, k_descale, v_descale : finite and > 0 (else FA_ERR_SCALE);
+ *           scale * q_descale * k_descale * log2(e) must be finite in fp32.
+ * stream  : HIP stream; NULL means the default stream.
+ *
+ * Ownership, validation and errors as fa_fwd: nothing is allocated, o and
+ * lse must not overlap the inputs (FA_ERR_ARG), FA_ERR_HIP carries the
+ * runtime's message in fa_hip_error_string().
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v,
+                     void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                     int causal, float scale, float q_descale, float k_descale, float v_descale,
+                     hipStream_t stream);
+
+/*
  * fa_bwd -- gradients of the exact attention forward, enqueued on `stream`.
  *
  * The backward that keeps only O and the per-row log-sum-exp from the forward

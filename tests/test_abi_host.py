@@ -211,3 +211,38 @@ def test_library_exports_nothing_undeclared(lib):
                          check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert exported == _declared_functions(), exported ^ _declared_functions()
+
+
+def fcall(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, Hq=1, Hkv=1, Tq=16, Tk=16, d=64, causal=1, scale=0.125,
+          qd=0.01, kd=0.02, vd=0.03):
+    return _lib.fa_fwd_fp8_raw(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, qd, kd, vd, 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fp8_null_pointer(lib, which):
+    assert fcall(**{which: 0}) == _lib.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _lib.FA_ERR_SHAPE), (dict(Tk=0), _lib.FA_ERR_SHAPE), (dict(Hq=3, Hkv=2), _lib.FA_ERR_SHAPE),
+    (dict(Tq=17, Tk=16), _lib.FA_ERR_SHAPE), (dict(d=96), _lib.FA_ERR_HEAD_DIM), (dict(d=32), _lib.FA_ERR_HEAD_DIM),
+    (dict(scale=math.inf), _lib.FA_ERR_SCALE), (dict(qd=0.0), _lib.FA_ERR_SCALE), (dict(kd=-1.0), _lib.FA_ERR_SCALE),
+    (dict(vd=math.nan), _lib.FA_ERR_SCALE), (dict(vd=math.inf), _lib.FA_ERR_SCALE),
+    (dict(scale=1e30, qd=1e10, kd=1e10), _lib.FA_ERR_SCALE), (dict(causal=3), _lib.FA_ERR_ARG),
+    (dict(q=A + 8), _lib.FA_ERR_ALIGN), (dict(o=4 * A + 4), _lib.FA_ERR_ALIGN), (dict(lse=5 * A + 1), _lib.FA_ERR_ALIGN),
+    (dict(o=A + 16), _lib.FA_ERR_ARG), (dict(lse=3 * A + 16), _lib.FA_ERR_ARG), (dict(o=4 * A, lse=4 * A + 64), _lib.FA_ERR_ARG),
+    (dict(Tq=1 << 31, Tk=1 << 31), _lib.FA_ERR_OVERFLOW), (dict(B=1 << 40, Hq=1 << 30, Hkv=1 << 30), _lib.FA_ERR_OVERFLOW),
+])
+def test_fp8_rejects(lib, kw, code):
+    assert fcall(**kw) == code
+    assert lib.fa_hip_error_string() == b""
+
+
+def test_fp8_python_wrapper_rejects_bf16_and_cpu():
+    import torch
+    x = torch.zeros((1, 1, 16, 64), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        _lib.fwd_fp8(x, x, x, True)                  # CPU tensors
+    y = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.fwd_fp8(y, y, y, True)                  # not E4M3 bytes

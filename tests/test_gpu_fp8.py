@@ -1,0 +1,333 @@
+"""GPU parity of the FP8 forward (``fa_fwd_fp8``, through the C ABI) against the oracle.
+
+Both sides consume the same seeded E4M3 bytes and descale factors; the oracle
+computes the exact attention of the dequantised operands in fp64.  The FP8
+forward rounds the probability weights to E4M3 before the PV product, so the
+tolerance is derived from that arithmetic, not taken from the bf16 forward:
+
+* every output element within ``1.01 * pv_error_bound_rows + 1e-6`` of the
+  oracle (the per-element bound of ``oracle.fp8``: the weights' rounding, the
+  FP8 matrix instruction's summation, fp32 accumulation, the bf16 store; 1%
+  covers the exponentials it leaves out);
+* the root of the summed squared error within the estimate
+  ``pv_error_rms_rows`` (an emulation of the rounding lands near 0.6 of it);
+* lse (fp32 weights) within 1e-3 plus the per-row bound on the scores' own
+  error (``score_error_rows``: the matrix instruction sums the 64 products of
+  a score block to within 2^-10 of the largest one).
+
+Closed forms need less: all-equal scores give weights of exactly 8, so Q = 0
+yields the running mean of V, and V = 1 yields v_descale exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8 as ofp8
+from exact_io_aware_13_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX_ABS = 1e-3
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_io_aware_13_amd as fa
+    fa.load()
+    oracle.build(force=False)
+    return fa
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev8(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).to("cuda:0")
+
+
+def run8(fa, q8, k8, v8, causal, scale, ds):
+    import torch
+    o, lse = fa.fwd_fp8(to_dev8(q8), to_dev8(k8), to_dev8(v8), causal, float(scale), ds)
+    torch.cuda.synchronize()
+    o = oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    return o, lse.cpu().numpy().astype(np.float64)
+
+
+def draw8(Bq, Bkv, seed, scale_q=1.0, spikes=False):
+    """Seeded float32 normals of shapes Bq (Q) and Bkv (K, V), quantised per tensor."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal(size=Bq, dtype=np.float32) * np.float32(scale_q)
+    k = rng.standard_normal(size=Bkv, dtype=np.float32)
+    v = rng.standard_normal(size=Bkv, dtype=np.float32)
+    if spikes:
+        q[rng.random(size=Bq[:3]) < 0.01] *= np.float32(8.0)
+        k[rng.random(size=Bkv[:3]) < 0.01] *= np.float32(8.0)
+    (q8, qd), (k8, kd), (v8, vd) = wl.quantize_e4m3(q), wl.quantize_e4m3(k), wl.quantize_e4m3(v)
+    return q8, k8, v8, (float(qd), float(kd), float(vd))
+
+
+def check8(o, lse, q8, k8, v8, ds, causal, scale, rows, label):
+    """Compare the GPU rows ``rows`` (flat indices) with the oracle and the derived tolerance."""
+    qf, kf, vf = ofp8.dequantize(q8, ds[0]), ofp8.dequantize(k8, ds[1]), ofp8.dequantize(v8, ds[2])
+    d = q8.shape[-1]
+    o_ref, lse_ref = oracle.attention_rows_f64(qf, kf, vf, causal, float(scale), rows)
+    bound = ofp8.pv_error_bound_rows(qf, kf, vf, causal, float(scale), rows)
+    rms_pred = ofp8.pv_error_rms_rows(qf, kf, vf, causal, float(scale), rows)
+    got = o.reshape(-1, d)[rows]
+    err = np.abs(got - o_ref)
+    ratio = float(np.max(err / (bound + 1e-30)))
+    rms = float(np.sqrt(np.sum(err ** 2)))
+    lse_err = np.abs(lse.reshape(-1)[rows] - lse_ref)
+    lse_tol = LSE_MAX_ABS + ofp8.score_error_rows(qf, kf, causal, float(scale), rows)
+    lse_abs = float(lse_err.max())
+    rel_l2 = float(np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
+    say(f"[{label}] {len(rows)} rows: O max-abs {err.max():.3e}, worst err/bound {ratio:.3f}, "
+        f"rms err / estimate {rms / max(rms_pred, 1e-30):.3f}, rel-L2 {rel_l2:.3e}, lse max-abs {lse_abs:.3e}")
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse.reshape(-1)[rows]))
+    bad = err > 1.01 * bound + 1e-6
+    assert not np.any(bad), (label, np.argwhere(bad)[:5], err[bad][:5], bound[bad][:5])
+    assert rms <= rms_pred, (label, rms, rms_pred)
+    assert np.all(lse_err <= lse_tol), (label, lse_abs, float(lse_tol[np.argmax(lse_err)]))
+
+
+def all_rows(q8):
+    return np.arange(int(np.prod(q8.shape[:3])), dtype=np.int64)
+
+
+def some_rows(q8, n, seed):
+    B, H, T, _ = q8.shape
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, 255, 256, T - 1]
+    rows = set()
+    for bh in rng.choice(B * H, size=min(4, B * H), replace=False):
+        rows.update(int(bh) * T + i for i in fixed if 0 <= i < T)
+        rows.update(int(bh) * T + int(i) for i in rng.choice(T, size=min(T, n // 4), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# (B, Hq, Hkv, Tq, Tk, d, causal): one tile, ragged tails, both head sizes,
+# grouped heads (folded and not), one query row, Tq < Tk.
+CASES = [
+    (1, 1, 1, 128, 128, 64, True), (1, 2, 2, 64, 64, 128, False), (2, 4, 4, 1000, 1000, 128, True),
+    (2, 3, 3, 777, 777, 64, False), (1, 8, 2, 520, 520, 128, True), (2, 8, 2, 300, 300, 64, False),
+    (1, 4, 1, 1, 2000, 128, True), (1, 2, 2, 130, 700, 128, True), (1, 1, 1, 1, 1, 64, True),
+    (1, 1, 1, 3, 3, 128, False), (2, 2, 2, 65, 65, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_every_row(fa, case):
+    B, Hq, Hkv, Tq, Tk, d, causal = case
+    say(f"case fp8 {case}")
+    q8, k8, v8, ds = draw8((B, Hq, Tq, d), (B, Hkv, Tk, d), seed=2000 + Tq + d)
+    scale = np.float32(1.0 / math.sqrt(d))
+    o, lse = run8(fa, q8, k8, v8, causal, scale, ds)
+    check8(o, lse, q8, k8, v8, ds, causal, scale, all_rows(q8), f"fp8 {case}")
+
+
+# Long rows: the 8-wave workgroup shape (T >= 8192 causal, >= 4096 unmasked), a
+# spiky draw (row scales x8 force rescales), on sampled rows.
+LONG = [((1, 2, 2, 8292, 8292, 128, True), False), ((1, 2, 2, 4200, 4200, 128, False), False),
+        ((1, 2, 2, 4096, 4096, 128, True), True), ((1, 2, 2, 3000, 3000, 64, True), True)]
+
+
+@pytest.mark.parametrize("case,spikes", LONG, ids=lambda c: "x".join(map(str, c)) if isinstance(c, tuple) else str(c))
+def test_long_rows_sampled(fa, case, spikes):
+    B, Hq, Hkv, Tq, Tk, d, causal = case
+    say(f"case fp8 long {case} spikes={spikes}")
+    q8, k8, v8, ds = draw8((B, Hq, Tq, d), (B, Hkv, Tk, d), seed=3000 + Tq, spikes=spikes)
+    scale = np.float32(1.0 / math.sqrt(d))
+    o, lse = run8(fa, q8, k8, v8, causal, scale, ds)
+    check8(o, lse, q8, k8, v8, ds, causal, scale, some_rows(q8, 256, Tq), f"fp8 long {case}")
+
+
+def test_workload_c4fp8_sampled_rows(fa):
+    """The benchmarked FP8 workload at full size, on the seeded sample rows."""
+    w = wl.BY_KEY["c4fp8"]
+    say(f"case {w.key}: {w.title}")
+    q8, k8, v8, ds = wl.workload_inputs_fp8(w)
+    scale = np.float32(w.scale)
+    o, lse = run8(fa, q8, k8, v8, w.causal, scale, ds)
+    check8(o, lse, q8, k8, v8, ds, w.causal, scale, wl.sample_rows(w), w.key)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_other_scales_and_descales(fa, scale):
+    say(f"case fp8 scale={scale}")
+    q8, k8, v8, _ = draw8((1, 2, 300, 64), (1, 2, 300, 64), seed=77)
+    ds = (0.013, 0.021, 0.5)
+    for causal in (True, False):
+        o, lse = run8(fa, q8, k8, v8, causal, np.float32(scale), ds)
+        check8(o, lse, q8, k8, v8, ds, causal, np.float32(scale), all_rows(q8), f"fp8 scale {scale} c={causal}")
+
+
+EXACT = [(1, 2, 2, 65, 65, 64, True), (1, 2, 2, 300, 300, 128, True), (1, 3, 3, 130, 130, 128, False),
+         (2, 2, 2, 777, 777, 64, True), (1, 2, 2, 8292, 8292, 128, True)]
+
+
+@pytest.mark.parametrize("case", EXACT, ids=lambda c: "x".join(map(str, c)))
+def test_exact_weights_every_row(fa, case):
+    """Scores that are whole numbers in exp2 units (scale = ln 2, Q = e_0, K = integers
+    0..-6 in dimension 0) give weights 8 * 2^-k, all exact in E4M3, so the kernel's
+    only errors are the bf16 store, the matrix instruction's summation and fp32
+    accumulation: any key whose weight met the wrong V row would show far above."""
+    B, Hq, Hkv, Tq, Tk, d, causal = case
+    say(f"case fp8 exact weights {case}")
+    rng = np.random.default_rng(4000 + Tq + d)
+    q = np.zeros((B, Hq, Tq, d))
+    q[..., 0] = 1.0
+    k = np.zeros((B, Hkv, Tk, d))
+    k[..., 0] = -rng.integers(0, 7, size=(B, Hkv, Tk))
+    v = rng.standard_normal((B, Hkv, Tk, d)).astype(np.float32)
+    q8, k8 = wl.f32_to_e4m3_bits(q), wl.f32_to_e4m3_bits(k)
+    v8, vd = wl.quantize_e4m3(v)
+    ds = (1.0, 1.0, float(vd))
+    scale = np.float32(math.log(2.0))
+    o, lse = run8(fa, q8, k8, v8, causal, scale, ds)
+    vf = ofp8.dequantize(v8, vd)
+    rows = all_rows(q8) if Tq <= 1000 else some_rows(q8, 512, Tq)
+    o_ref, lse_ref = oracle.attention_rows_f64(ofp8.widen_e4m3(q8), ofp8.widen_e4m3(k8), vf, causal,
+                                               float(scale), rows)
+    got = o.reshape(-1, d)[rows]
+    worst = 0.0
+    for n_i, r in enumerate(rows):
+        bh, i = divmod(int(r), Tq)
+        b, h = divmod(bh, Hq)
+        hk = h // (Hq // Hkv)
+        nv = min(Tk, i + Tk - Tq + 1) if causal else Tk
+        s = k[b, hk, :nv, 0] * float(scale)
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        wv = w @ np.abs(vf[b, hk, :nv])
+        ref = o_ref[n_i]
+        tol = (2.0 ** -8 * np.abs(ref) + ofp8.KAPPA_MFMA * (1 + 2.0 ** -4) * (wv + np.abs(ref))
+               + 2.0 * nv * 2.0 ** -24 * wv + 1e-6)
+        e = np.abs(got[n_i] - ref)
+        worst = max(worst, float(np.max(e / tol)))
+        assert np.all(e <= tol), (case, int(r), float(e.max()), float(tol[np.argmax(e)]))
+    lse_abs = float(np.abs(lse.reshape(-1)[rows] - lse_ref).max())
+    say(f"[fp8 exact weights {case}] worst err/tol {worst:.3f}, lse max-abs {lse_abs:.3e}")
+    assert lse_abs <= LSE_MAX_ABS
+
+
+def test_zero_queries_running_mean_full_size(fa):
+    """Q = 0: every weight is exactly 8, so causal O_i is the mean of V_0..V_i
+    (to the matrix instruction's summation, fp32 accumulation and the bf16
+    store) and lse_i = ln(i + 1)."""
+    w = wl.BY_KEY["c4fp8"]
+    say(f"case fp8 Q=0 closed form at {w.shape}")
+    _, k8, v8, ds = wl.workload_inputs_fp8(w)
+    q8 = np.zeros((w.B, w.H, w.T, w.d), dtype=np.uint8)
+    o, lse = run8(fa, q8, k8, v8, True, np.float32(w.scale), ds)
+    n = np.arange(1, w.T + 1, dtype=np.float64)
+    vflat = ofp8.dequantize(v8, ds[2]).reshape(w.B * w.H, w.T, w.d)
+    oflat = o.reshape(w.B * w.H, w.T, w.d)
+    worst = 0.0
+    for bh in range(w.B * w.H):
+        ref = np.cumsum(vflat[bh], axis=0) / n[:, None]
+        mean_abs = np.cumsum(np.abs(vflat[bh]), axis=0) / n[:, None]
+        tol = (2.0 ** -8 * np.abs(ref) + 2.0 * n[:, None] * 2.0 ** -24 * np.abs(vflat[bh]).max()
+               + ofp8.KAPPA_MFMA * (mean_abs + np.abs(ref)) + 1e-7)
+        e = np.abs(oflat[bh] - ref)
+        worst = max(worst, float(e.max()))
+        assert np.all(e <= tol), (bh, float(e.max()))
+    lse_err = float(np.abs(lse.reshape(w.B * w.H, w.T) - np.log(n)[None]).max())
+    say(f"[fp8 Q=0] O max-abs {worst:.3e} lse max-abs {lse_err:.3e}")
+    assert lse_err <= LSE_MAX_ABS
+
+
+def test_ones_values_give_the_descale_full_size(fa):
+    """V = 1 (E4M3 0x38): the PV product and the weight sum see the same
+    operands, so O = v_descale exactly."""
+    w = wl.BY_KEY["c4fp8"]
+    say(f"case fp8 V=1 closed form at {w.shape}")
+    q8, k8, _, ds = wl.workload_inputs_fp8(w)
+    v8 = np.full_like(q8, 0x38)
+    o, lse = run8(fa, q8, k8, v8, True, np.float32(w.scale), (ds[0], ds[1], 0.375))
+    assert np.all(o == 0.375)
+    assert np.all(np.isfinite(lse))
+
+
+def test_causal_row0_closed_form(fa):
+    """Row 0 sees only key 0: its one weight is 8 (exact), O_0 = v_descale * V_0 and
+    lse_0 = scale q_0 . k_0 (descaled), within the scores' own error."""
+    w = wl.BY_KEY["c4fp8"]
+    q8, k8, v8, ds = wl.workload_inputs_fp8(w)
+    scale = np.float32(w.scale)
+    o, lse = run8(fa, q8, k8, v8, True, scale, ds)
+    v0 = ofp8.dequantize(v8[:, :, 0], ds[2])
+    want = oracle.widen_bf16(wl.f32_to_bf16_bits(v0.astype(np.float32)))
+    assert np.array_equal(o[:, :, 0], want)
+    q0, k0 = ofp8.dequantize(q8[:, :, 0], ds[0]), ofp8.dequantize(k8[:, :, 0], ds[1])
+    rows0 = np.arange(w.B * w.H) * w.T
+    qf, kf = ofp8.dequantize(q8, ds[0]), ofp8.dequantize(k8, ds[1])
+    tol = LSE_MAX_ABS + ofp8.score_error_rows(qf, kf, True, float(scale), rows0).reshape(w.B, w.H)
+    assert np.all(np.abs(lse[:, :, 0] - float(scale) * np.sum(q0 * k0, axis=-1)) <= tol)
+
+
+def _embed8(rows, d):
+    rows = np.asarray(rows, dtype=np.float64)
+    out = np.zeros((1, 1, rows.shape[0], d))
+    out[0, 0, :, :rows.shape[1]] = rows
+    return wl.f32_to_e4m3_bits(out)
+
+
+def test_w1_three_token_example(fa):
+    """'A three-token example' (Q = K = 0, V rows [10, 0], [0, 20], [30, 30]), zero-padded."""
+    import pins
+    g = pins.golden("w1_three_token_causal.json")
+    for d in (64, 128):
+        q8, k8, v8 = _embed8(g["q"], d), _embed8(g["k"], d), _embed8(g["v"], d)
+        o, lse = run8(fa, q8, k8, v8, True, np.float32(0.7), (1.0, 1.0, 1.0))
+        exact = np.array([[10.0, 0.0], [5.0, 10.0], [40.0 / 3.0, 50.0 / 3.0]])
+        want = oracle.widen_bf16(wl.f32_to_bf16_bits(exact.astype(np.float32)))
+        assert np.array_equal(o[0, 0, :, :2], want), o[0, 0, :, :2]
+        assert np.all(o[0, 0, :, 2:] == 0.0)
+        assert np.allclose(lse[0, 0], [0.0, math.log(2), math.log(3)], atol=1e-6, rtol=0)
+
+
+def test_w2_four_scores_example(fa):
+    """Step 2's worked example: scores [2, 1, 4, 3], values [10, 20, 30, 40] -> 30.3054,
+    all exact in E4M3; the FP8 weights keep the result within the derived bound."""
+    import pins
+    g = pins.golden("w2_four_scores.json")
+    s = np.asarray(g["scores"])
+    q = np.zeros((4, 1)); q[:, 0] = 8.0
+    k = s[:, None]; v = np.asarray(g["values"])[:, None]
+    q8, k8, v8 = _embed8(q, 64), _embed8(k, 64), _embed8(v, 64)
+    o, lse = run8(fa, q8, k8, v8, True, np.float32(0.125), (1.0, 1.0, 1.0))
+    check8(o, lse, q8, k8, v8, (1.0, 1.0, 1.0), True, np.float32(0.125), np.arange(4), "fp8 w2")
+    assert abs(o[0, 0, 3, 0] - g["output"]) <= 1.0   # 30.3054, within the E4M3-weight error
+    assert o[0, 0, 0, 0] == 10.0
+    assert abs(lse[0, 0, 3] - (4.0 + math.log(g["combine"]["denominator"]))) <= 5e-4
+
+
+def test_deterministic(fa):
+    import torch
+    q8, k8, v8, ds = draw8((2, 4, 1024, 128), (2, 4, 1024, 128), seed=9)
+    q, k, v = to_dev8(q8), to_dev8(k8), to_dev8(v8)
+    o1, l1 = fa.fwd_fp8(q, k, v, True, None, ds)
+    o2, l2 = fa.fwd_fp8(q, k, v, True, None, ds)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_side_stream_and_preallocated_outputs(fa):
+    import torch
+    q8, k8, v8, ds = draw8((2, 3, 333, 128), (2, 3, 333, 128), seed=5)
+    q, k, v = to_dev8(q8), to_dev8(k8), to_dev8(v8)
+    o = torch.full((2, 3, 333, 128), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.full((2, 3, 333), float("nan"), device="cuda:0")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fa.fwd_fp8_out(q, k, v, o, lse, False, None, ds)
+    s.synchronize()
+    o_ref, lse_ref = fa.fwd_fp8(q, k, v, False, None, ds)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, lse_ref)

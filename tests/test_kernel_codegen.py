@@ -90,3 +90,45 @@ def test_backward_lds_reads_do_not_wait_on_tile_loads(asm_bwd):
         waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
                  if a.startswith("s_waitcnt") and "vmcnt" in a and "lgkmcnt" not in a and b.startswith("ds_read")]
         assert not waits, (name, [body[i:i + 2] for i in waits[:3]])
+
+
+@pytest.fixture(scope="module")
+def asm_fp8(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "fa_fwd_fp8.s"
+    cmd = [build.hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + \
+        ["--cuda-device-only", "-S", "-o", str(out), build.SRCS[2]]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _fp8_kernels(asm):
+    for m in re.finditer(r"^(_ZN\S*fa_fwd_fp8_kernel\S*):", asm, re.M):
+        start = m.end()
+        end = asm.index(".Lfunc_end", start)
+        body = [l.strip() for l in asm[start:end].splitlines()]
+        yield m.group(1), [l for l in body if l and not l.startswith((";", "."))]
+
+
+def test_fp8_variants_use_the_fp8_matrix_cores(asm_fp8):
+    kernels = dict(_fp8_kernels(asm_fp8))
+    assert len(kernels) == 6, list(kernels)   # (d=128 x causal x wave groups) + (d=64 x causal)
+    for name, body in kernels.items():
+        ops = [l.split()[0] for l in body]
+        assert "v_mfma_f32_32x32x64_f8f6f4" in ops, name
+        assert "ds_read_b64_tr_b8" in ops and "v_cvt_pk_fp8_f32" in ops, name
+        assert not any(o.startswith("v_mfma") and "f8f6f4" not in o for o in ops), name
+
+
+def test_fp8_no_register_spills_and_two_waves_per_simd(asm_fp8):
+    spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm_fp8)]
+    assert spills and max(spills) == 0
+    counts = [int(x) for x in re.findall(r"\.vgpr_count:\s+(\d+)", asm_fp8)]
+    assert max(counts) <= 256, counts
+
+
+def test_fp8_lds_reads_do_not_wait_on_tile_loads(asm_fp8):
+    for name, body in _fp8_kernels(asm_fp8):
+        waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
+                 if a.startswith("s_waitcnt") and "vmcnt" in a and "lgkmcnt" not in a and b.startswith("ds_read")]
+        assert not waits, (name, [body[i:i + 2] for i in waits[:3]])
+
