@@ -9,8 +9,11 @@ tolerance is derived from that arithmetic, not taken from the bf16 forward:
   oracle (the per-element bound of ``oracle.fp8``: the weights' rounding, the
   FP8 matrix instruction's summation, fp32 accumulation, the bf16 store; 1%
   covers the exponentials it leaves out);
-* the root of the summed squared error within the estimate
-  ``pv_error_rms_rows`` (an emulation of the rounding lands near 0.6 of it);
+* the root of the summed squared error within 1.5 times the estimate
+  ``pv_error_rms_rows`` (an expectation, not a bound: an emulation of the
+  rounding lands near 0.6 of it, and rows whose weights are nearly one-hot,
+  as in the spiky draws, make the sum of squares heavy-tailed; measured
+  0.05-0.9);
 * lse (fp32 weights) within 1e-3 plus the per-row bound on the scores' own
   error (``score_error_rows``: the matrix instruction sums the 64 products of
   a score block to within 2^-10 of the largest one).
@@ -92,7 +95,7 @@ def check8(o, lse, q8, k8, v8, ds, causal, scale, rows, label):
     assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse.reshape(-1)[rows]))
     bad = err > 1.01 * bound + 1e-6
     assert not np.any(bad), (label, np.argwhere(bad)[:5], err[bad][:5], bound[bad][:5])
-    assert rms <= rms_pred, (label, rms, rms_pred)
+    assert rms <= 1.5 * rms_pred, (label, rms, rms_pred)
     assert np.all(lse_err <= lse_tol), (label, lse_abs, float(lse_tol[np.argmax(lse_err)]))
 
 
