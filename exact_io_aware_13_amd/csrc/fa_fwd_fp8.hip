@@ -340,14 +340,24 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
     };
 
     f32x16 sc[2];
-    i32x8 pk;   // E4M3 weights of the current tile, consumed by the next matrix phase
+    // fp32 weights of the current tile.  The next matrix phase converts them
+    // to E4M3 (the conversion hides under its first LDS reads): with FP8
+    // products the matrix phase is the shorter one, and moving this VALU work
+    // there keeps a wave's softmax phase from outlasting its partner's matrix
+    // phase (the two waves of a SIMD then contend less for the VALU).
+    float pw[32];
 
     auto matrix_phase = [&] __device__ (int j, auto parity) {
         constexpr int P = decltype(parity)::value;
         __builtin_amdgcn_s_setprio(1);
         const bool do_pv = j >= 0 && j < n_w;
         const bool do_qk = j + 1 < n_w;
-        if (do_pv) pv(vslot[P], pk);
+        if (do_pv) {
+            i32x8 pk;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) pk[n] = pack_e4m3x4(pw[4 * n], pw[4 * n + 1], pw[4 * n + 2], pw[4 * n + 3]);
+            pv(vslot[P], pk);
+        }
         if (do_qk) qk(kslot[P ^ 1], sc);
         __builtin_amdgcn_s_setprio(0);
     };
@@ -385,7 +395,7 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
         }
         st.l32 += ts;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) pk[n] = pack_e4m3x4(p[4 * n], p[4 * n + 1], p[4 * n + 2], p[4 * n + 3]);
+        for (int n = 0; n < 32; ++n) pw[n] = p[n];
     };
 
     using Even = std::integral_constant<int, 0>;
