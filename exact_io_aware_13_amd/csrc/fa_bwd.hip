@@ -504,6 +504,10 @@ __global__ __launch_bounds__(512) void fa_bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ kernel.  LDS per slot: K tile, V tile.
+// Operand reads the dQ kernel keeps in flight ahead of the MFMAs (3-6 measured alike).
+#ifndef FB_DQ_AHEAD
+#define FB_DQ_AHEAD 4
+#endif
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ DO,
@@ -596,42 +600,79 @@ __device__ __forceinline__ void dq_block(const uint16_t* __restrict__ Q, const u
                 s[kb][i] = 0.0f;
                 dp[kb][i] = 0.0f;
             }
+        // S^T = K Q^T and dP^T = V dO^T, the K and V operand reads interleaved
+        // and kAhead of them kept in flight ahead of the MFMA that uses them.
+        {
+            constexpr int N = 4 * G::kDSteps;   // operands: (step, key block, K or V)
+            bf16x8 op[N];
 #pragma unroll
-        for (int st = 0; st < G::kDSteps; ++st)
+            for (int i = 0; i < N; ++i)
+                op[i] = row_operand<D>((i & 1) ? vs : ks, to, (i >> 1) & 1, i >> 2);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(ks, to, kb, st), qf[st], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vs, to, kb, st), df[st], dp[kb], 0, 0,
-                                                                 0);
+            for (int i = 0; i < N; ++i) {
+                const int kb = (i >> 1) & 1, st = i >> 2;
+                if (i & 1) dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], df[st], dp[kb], 0, 0, 0);
+                else s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[st], s[kb], 0, 0, 0);
             }
+            constexpr int kAhead = FB_DQ_AHEAD < N ? FB_DQ_AHEAD : N;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+            for (int i = 0; i < N - kAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        }
         // Element i of key block kb is key 64 j + 32 kb + 8 (i / 4) + 4 half + i % 4.
-        const bool masked = j >= j_mask;
-        const int key0 = j * kRows;
+        // Exponent arguments first; only a wave's last tiles can hold keys a row
+        // must not see, and there they are set to -inf (P = 0) in place.
+        float x[2][16];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[kb][i] = __builtin_fmaf(s[kb][i], c, -lse2);
+        if (j >= j_mask) {
+            const int key0 = j * kRows;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kj = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool vis = kj < Tk && (!CAUSAL || kj <= qrow + off);
+                    x[kb][i] = vis ? x[kb][i] : -INFINITY;
+                }
+        }
         uint32_t dsp[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             float dsv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -lse2));
-                if (masked) {
-                    const int kj = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool vis = kj < Tk && (!CAUSAL || kj <= qrow + off);
-                    pv = vis ? pv : 0.0f;
-                }
-                dsv[i] = pv * (dp[kb][i] - dd);
-            }
+            for (int i = 0; i < 16; ++i) dsv[i] = __builtin_amdgcn_exp2f(x[kb][i]) * (dp[kb][i] - dd);
 #pragma unroll
             for (int n = 0; n < 8; ++n) dsp[kb][n] = pack_bf16x2(dsv[2 * n], dsv[2 * n + 1]);
         }
-        // dQ^T += K^T dS^T over the tile's 64 keys (4 steps of 16).
+        // dQ^T += K^T dS^T over the tile's 64 keys (4 steps of 16); each operand
+        // is two transposed reads, kAhead operands kept in flight.
+        {
+            constexpr int N = 4 * G::kDBlocks;
+            bf16x8 op[N];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int kb = st >> 1, h8 = 4 * (st & 1);
-            const bf16x8 sb = as_bf16x8(dsp[kb][h8], dsp[kb][h8 + 1], dsp[kb][h8 + 2], dsp[kb][h8 + 3]);
+            for (int i = 0; i < N; ++i) op[i] = tr_operand<D>(ks, to, i / G::kDBlocks, i % G::kDBlocks);
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db)
-                dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(ks, to, st, db), sb, dqa[db], 0, 0, 0);
+            for (int i = 0; i < N; ++i) {
+                const int st = i / G::kDBlocks, db = i % G::kDBlocks;
+                const int kb = st >> 1, h8 = 4 * (st & 1);
+                const bf16x8 sb = as_bf16x8(dsp[kb][h8], dsp[kb][h8 + 1], dsp[kb][h8 + 2], dsp[kb][h8 + 3]);
+                dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], sb, dqa[db], 0, 0, 0);
+            }
+            constexpr int kAhead = FB_DQ_AHEAD < N ? FB_DQ_AHEAD : N;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+            for (int i = 0; i < N - kAhead; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
         }
     };
 
