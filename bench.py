@@ -305,9 +305,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     # The clock settles only after a few dozen back-to-back launches (the first
-    # ~40 show a power-management transient), so the default warm-up covers it.
+    # ~40 show a power-management transient); 200 warm-up launches (0.1 s at
+    # c4) reach the steady state.
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=wl.BENCH_KEY, choices=sorted(wl.BY_KEY))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
