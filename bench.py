@@ -245,9 +245,12 @@ def bench_fp8(args, w: wl.Workload, dev) -> int:
     lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
     scale = float(np.float32(w.scale))
     descales = tuple(float(x) for x in ds)
+    n_split = w.n_split if w.n_split is not None else fa.split_count(w.B, w.H, w.Hkv, w.T, w.Tk, w.d, w.causal)
+    ws_bytes = fa.split_workspace_bytes(w.B, w.H, w.T, w.Tk, w.d, n_split)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
-        fa.fwd_fp8_out(q, k, v, o, lse, w.causal, scale, descales)
+        fa.fwd_fp8_out(q, k, v, o, lse, w.causal, scale, descales, n_split=n_split, workspace=workspace)
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
@@ -268,19 +271,31 @@ def bench_fp8(args, w: wl.Workload, dev) -> int:
     ms_per_step = wall_ms / args.steps
     assert torch.isfinite(lse).all().item(), "non-finite lse"
     flops = w.flops()
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-            "traffic": measured_traffic(w.key, FP8_TRAFFIC_FILE, FP8_SRC),
-            "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": w.algorithmic_bytes()}
-    config = {"workload": w.title, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "causal": w.causal,
-              "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
-              "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)}
+    hbm_bound = w.algorithmic_bytes() * PEAK_FP8_TFLOPS * 1e12 > flops * PEAK_HBM_GBS * 1e9
+    config = {"workload": w.title, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "causal": w.causal}
+    if w.Hkv != w.H or w.Tk != w.T or n_split != 1:
+        config.update({"Hkv": w.Hkv, "Tk": w.Tk, "n_split": n_split})
+    if hbm_bound:
+        gbs = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
+        value, unit = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        metric = f"attention fwd GB/s, {w.title}"
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 4),
+                "flops": flops}
+    else:
+        value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        metric = f"attention fwd TFLOP/s and % of fp8 MFMA peak, {w.title}"
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                "traffic": measured_traffic(w.key, FP8_TRAFFIC_FILE, FP8_SRC),
+                "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": w.algorithmic_bytes()}
+        config.update({"pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+                       "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)})
     out = {
-        "metric": f"attention fwd TFLOP/s and % of fp8 MFMA peak, {w.title}",
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -25,7 +25,7 @@ FA_ERR_HIP = 7
 FA_ERR_ARG = 8
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
-            "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
+            "fa_fwd_fp8", "fa_fwd_fp8_split", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
 
 _lib = None
 
@@ -60,6 +60,9 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, f32, f32, f32,
                                    f32, vp]
         lib.fa_fwd_fp8.restype = ctypes.c_int
+        lib.fa_fwd_fp8_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, f32, f32, f32,
+                                         f32, i64, vp, ctypes.c_size_t, vp]
+        lib.fa_fwd_fp8_split.restype = ctypes.c_int
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                ctypes.c_float, vp, ctypes.c_size_t, vp]
         lib.fa_bwd.restype = ctypes.c_int
@@ -113,6 +116,15 @@ def fa_fwd_fp8_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
     """Call ``fa_fwd_fp8`` with raw addresses; returns the fa_status code."""
     return int(load().fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
                                  float(scale), float(q_descale), float(k_descale), float(v_descale), stream))
+
+
+def fa_fwd_fp8_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
+                         Tq: int, Tk: int, d: int, causal: int, scale: float, q_descale: float, k_descale: float,
+                         v_descale: float, n_split: int, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """Call ``fa_fwd_fp8_split`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd_fp8_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
+                                       float(scale), float(q_descale), float(k_descale), float(v_descale),
+                                       int(n_split), ws_ptr, ws_bytes, stream))
 
 
 def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int, dq_ptr: int,
@@ -238,12 +250,16 @@ def _check_fp8_tensors(q, k, v):
         raise ValueError("q, k, v must be on the same device")
 
 
-def fwd_fp8_out(q, k, v, o, lse, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0)) -> None:
+def fwd_fp8_out(q, k, v, o, lse, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0),
+                n_split: int | None = 1, workspace=None) -> None:
     """FP8 forward into caller buffers ``o`` (bf16, shaped like q) and ``lse`` (fp32, (B, Hq, Tq)).
 
     ``q``: (B, Hq, Tq, d), ``k, v``: (B, Hkv, Tk, d), E4M3 bytes (uint8 or
     float8_e4m3fn); ``descales`` = (q_descale, k_descale, v_descale), the
-    operands being ``descale * e4m3``.  Calls ``fa_fwd_fp8``.
+    operands being ``descale * e4m3``.  ``n_split`` = 1 calls ``fa_fwd_fp8``;
+    otherwise ``fa_fwd_fp8_split`` with a workspace as for ``fwd_out`` (``None``
+    asks the library for a split count; a workspace is allocated here if not
+    given).
     """
     import torch
     _check_fp8_tensors(q, k, v)
@@ -256,14 +272,27 @@ def fwd_fp8_out(q, k, v, o, lse, causal: bool, scale: float | None = None, desca
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     qd, kd, vd = (float(x) for x in descales)
+    if n_split is None:
+        n_split = split_count(B, Hq, Hkv, Tq, Tk, d, causal)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = fa_fwd_fp8_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
-                            Tq, Tk, d, int(bool(causal)), float(scale), qd, kd, vd, stream)
-        _check(st, "fa_fwd_fp8")
+        if n_split == 1:
+            st = fa_fwd_fp8_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                                Tq, Tk, d, int(bool(causal)), float(scale), qd, kd, vd, stream)
+            _check(st, "fa_fwd_fp8")
+            return
+        need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else 0
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        st = fa_fwd_fp8_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                                  Tq, Tk, d, int(bool(causal)), float(scale), qd, kd, vd, int(n_split), ws_ptr,
+                                  ws_bytes, stream)
+        _check(st, "fa_fwd_fp8_split")
 
 
-def fwd_fp8(q, k, v, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0)):
+def fwd_fp8(q, k, v, causal: bool, scale: float | None = None, descales=(1.0, 1.0, 1.0), n_split: int | None = 1):
     """FP8 E4M3 attention forward; returns ``(o, lse)`` with ``o`` bf16 and
     ``lse`` float32 (B, Hq, Tq).  Arguments as ``fwd_fp8_out``."""
     import torch
@@ -271,7 +300,7 @@ def fwd_fp8(q, k, v, causal: bool, scale: float | None = None, descales=(1.0, 1.
     B, Hq, Tq, d = q.shape
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
-    fwd_fp8_out(q, k, v, o, lse, causal, scale, descales)
+    fwd_fp8_out(q, k, v, o, lse, causal, scale, descales, n_split)
     return o, lse
 
 

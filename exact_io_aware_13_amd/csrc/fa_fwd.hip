@@ -708,19 +708,10 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (n_eff == 1) {
         err = d == 128 ? launch_d<128, false>(a, causal, ng, stream) : launch_d<64, false>(a, causal, ng, stream);
     } else {
+        if (rows > static_cast<int64_t>(INT32_MAX) * (256 / (d / 4))) return FA_ERR_OVERFLOW;   // combine grid
         err = d == 128 ? launch_d<128, true>(a, causal, ng, stream) : launch_d<64, true>(a, causal, ng, stream);
-        if (err == hipSuccess) {
-            const int rpb = static_cast<int>(256 / (d / 4));
-            const int64_t blocks = (rows + rpb - 1) / rpb;
-            if (blocks > INT32_MAX) return FA_ERR_OVERFLOW;
-            if (d == 128)
-                hipLaunchKernelGGL(fa_combine_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                                   a.op, a.lp, a.o, lse, rows, a.n_split);
-            else
-                hipLaunchKernelGGL(fa_combine_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                                   a.op, a.lp, a.o, lse, rows, a.n_split);
-            err = hipGetLastError();
-        }
+        if (err == hipSuccess)
+            err = fa_internal::launch_split_combine(a.op, a.lp, a.o, lse, rows, a.n_split, static_cast<int>(d), stream);
     }
     if (err != hipSuccess) {
         fa_internal::record_hip_error(err);
@@ -741,6 +732,19 @@ void record_hip_error(hipError_t err) {
 }
 
 void clear_hip_error() { g_hip_error[0] = '\0'; }
+
+hipError_t launch_split_combine(const float* op, const float* lp, uint16_t* o, float* lse, long long rows, int n_split,
+                                int d, hipStream_t stream) {
+    const int rpb = 256 / (d / 4);   // rows per 256-thread block
+    const long long blocks = (rows + rpb - 1) / rpb;
+    if (d == 128)
+        hipLaunchKernelGGL(fa_combine_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, op, lp, o,
+                           lse, rows, n_split);
+    else
+        hipLaunchKernelGGL(fa_combine_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, op, lp, o,
+                           lse, rows, n_split);
+    return hipGetLastError();
+}
 
 }  // namespace fa_internal
 

@@ -177,22 +177,29 @@ __device__ __forceinline__ void maybe_rescale8(WaveState8<D>& st, float m_new) {
     }
 }
 
-// Launch arguments; head mapping and causal alignment as for the bf16 forward.
+// Launch arguments; head mapping, causal alignment and key splits as for the
+// bf16 forward: key range [s * chunk, (s + 1) * chunk) goes to split s, and
+// with SPLIT the workgroup writes that split's normalised fp32 output and
+// log-sum-exp to op / lp for the combine kernel.
 struct Fwd8Args {
     const uint8_t* q;
     const uint8_t* k;
     const uint8_t* v;
     uint16_t* o;
     float* lse;
-    int tq, tk, n_qt, total, hq, group;
+    float* op;     // [n_split][rows][D]
+    float* lp;     // [n_split][rows]
+    long long rows;
+    int tq, tk, n_qt, total, hq, group, chunk, n_split;
     float c;        // scale * q_descale * k_descale * log2(e)
     float vscale;   // v_descale
 };
 
-template <int D, bool CAUSAL, int NG>
+template <int D, bool CAUSAL, int NG, bool SPLIT>
 __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                               const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
-                                              float* __restrict__ LSE, const Fwd8Args& a, FA_LDS char* const lds) {
+                                              float* __restrict__ LSE, float* __restrict__ OP, float* __restrict__ LP,
+                                              const Fwd8Args& a, FA_LDS char* const lds) {
     using G = Geo8<D, NG>;
     constexpr int kBM = G::kBM;
     const int Tq = a.tq, Tk = a.tk, n_qt = a.n_qt, total = a.total;
@@ -211,10 +218,11 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
     const int xcd = id % kXcds, xslot = id / kXcds;
     const int q8 = total / kXcds, r8 = total % kXcds;
     const int w = xcd < r8 ? xcd * (q8 + 1) + xslot : r8 * (q8 + 1) + (xcd - r8) * q8 + xslot;
-    int bh = w / n_qt;
+    int bh = w / (n_qt * a.n_split);
+    const int split = (w / n_qt) % a.n_split;
     int qt = CAUSAL ? n_qt - 1 - (w % n_qt) : (w % n_qt);
     constexpr int kRoundSlots = 256 * (NG == 2 ? 1 : 2);
-    if (CAUSAL && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
+    if (CAUSAL && a.n_split == 1 && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
         const int hx = q8 / n_qt;
         bh = xcd * hx + xslot % hx;
         qt = n_qt - 1 - xslot / hx;
@@ -230,12 +238,14 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
     const int qw0 = qt * kBM + blk * 32;
     const int qrow = qw0 + col;
     const int off = Tk - Tq;
-    const int k_hi = Tk;
+    const int k_lo = split * a.chunk;
+    const int k_hi = min(Tk, k_lo + a.chunk);
     const int kv_end = CAUSAL ? min(k_hi, min(Tq, qt * kBM + kBM) + off) : k_hi;
-    const int n_kt = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
-    const int w_end = CAUSAL ? min(k_hi, qw0 + 32 + off) : k_hi;
-    const int n_w = qw0 >= Tq || w_end <= 0 ? 0 : (w_end + kBN - 1) / kBN;
-    const int j_mask = CAUSAL ? min(n_w - 1, max(0, (qw0 + off + 1) / kBN)) : n_w - 1;
+    const int n_kt = kv_end > k_lo ? (kv_end - k_lo + kBN - 1) / kBN : 0;   // tiles the workgroup loads
+    const int w_end = CAUSAL ? min(k_hi, qw0 + 32 + off) : k_hi;            // keys this wave may see
+    const int n_w = qw0 >= Tq || w_end <= k_lo ? 0 : (w_end - k_lo + kBN - 1) / kBN;
+    // Tiles from j_mask on can hold keys some row of the wave must not see.
+    const int j_mask = CAUSAL ? min(n_w - 1, max(0, (qw0 + off + 1 - k_lo) / kBN)) : n_w - 1;
 
     uint32_t goff[G::kLoads];
 #pragma unroll
@@ -271,7 +281,7 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
             voff[db] = r * G::kRowBytes + 16 * ((2 * db + (g & 1)) ^ swz8<D>(r)) + 8 * (i & 1);
     }
 
-    if (n_kt > 0) load_tile(kbh, 0, kslot[0]);
+    if (n_kt > 0) load_tile(kbh, k_lo, kslot[0]);
 
     // Q^T operand (B of S^T): Q row qrow, bytes 64 s + 32 half + [0, 32); zeros past Tq.
     i32x8 qf[G::kDSteps];
@@ -364,7 +374,7 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
     auto softmax_phase = [&] __device__ (int j) {
         if (j < 0 || j >= n_w) return;
         if (j >= j_mask) {
-            const int key0 = j * kBN;
+            const int key0 = k_lo + j * kBN;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -406,8 +416,8 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
             const int j = ph >> 1;
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loads of phase ph - 2 have landed
             __syncthreads();
-            if (j + 1 < n_kt) load_tile(kbh, (j + 1) * kBN, kslot[(j + 1) & 1]);
-            if (j < n_kt) load_tile(vbh, j * kBN, vslot[j & 1]);
+            if (j + 1 < n_kt) load_tile(kbh, k_lo + (j + 1) * kBN, kslot[(j + 1) & 1]);
+            if (j < n_kt) load_tile(vbh, k_lo + j * kBN, vslot[j & 1]);
         }
     };
     if (grp == 0) {
@@ -442,12 +452,33 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
         }
     }
 
-    // Epilogue: O = v_descale * o / l8, lse = ln2 * (m + log2 l32).
-    if (n_w == 0) return;
+    // Epilogue: O = v_descale * o / l8, lse = ln2 * (m + log2 l32).  A row that
+    // saw no key (possible only for one split of a split problem) gets O = 0,
+    // lse = -inf.
     const float l32 = xhalf_sum(st.l32);
     const float l8 = st.l8[0];
     const float inv = l8 > 0.0f ? a.vscale / l8 : 0.0f;
     const float lse_row = kLn2 * (st.m + __builtin_amdgcn_logf(l32));
+    if constexpr (SPLIT) {
+        // Every row of the split is written, also those that saw no key.
+        const size_t prow = (size_t)split * (size_t)a.rows + (size_t)bh * Tq;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(OP + prow * D, (uint32_t)Tq * D * 4u);
+        const uint32_t prow_b = (uint32_t)qrow * D * 4u;
+#pragma unroll
+        for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x4 wv = {as_u32(st.o[b][4 * g + 0] * inv), as_u32(st.o[b][4 * g + 1] * inv),
+                            as_u32(st.o[b][4 * g + 2] * inv), as_u32(st.o[b][4 * g + 3] * inv)};
+                __builtin_amdgcn_raw_buffer_store_b128(wv, rp, prow_b + 4 * (b * 32 + 8 * g + 4 * half), 0, 0);
+            }
+        if (half == 0) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(LP + prow, (uint32_t)Tq * 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+        }
+        return;
+    }
+    if (n_w == 0) return;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + qbase, (uint32_t)Tq * D * 2u);
     const uint32_t orow = (uint32_t)qrow * D * 2u;
 #pragma unroll
@@ -465,11 +496,11 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
     }
 }
 
-template <int D, bool CAUSAL, int NG>
+template <int D, bool CAUSAL, int NG, bool SPLIT>
 __global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fp8_kernel(Fwd8Args a) {
     __shared__ __attribute__((aligned(1024))) char smem[Geo8<D, NG>::kLdsBytes];
-    fa_fwd8_block<D, CAUSAL, NG>(a.q, a.k, a.v, a.o, a.lse, a, (FA_LDS char*)smem);
+    fa_fwd8_block<D, CAUSAL, NG, SPLIT>(a.q, a.k, a.v, a.o, a.lse, a.op, a.lp, a, (FA_LDS char*)smem);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -477,28 +508,47 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <int D, bool CAUSAL, int NG>
+template <int D, bool CAUSAL, int NG, bool SPLIT>
 hipError_t launch8(const Fwd8Args& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, NG>), dim3(a.total), dim3(Geo8<D, NG>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, NG, SPLIT>), dim3(a.total), dim3(Geo8<D, NG>::kThreads), 0, stream,
+                       a);
     return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch8_d(const Fwd8Args& a, int64_t d, bool causal, int ng, hipStream_t stream) {
+    if (d == 128) {
+        if (ng == 2) return causal ? launch8<128, true, 2, SPLIT>(a, stream) : launch8<128, false, 2, SPLIT>(a, stream);
+        return causal ? launch8<128, true, 1, SPLIT>(a, stream) : launch8<128, false, 1, SPLIT>(a, stream);
+    }
+    return causal ? launch8<64, true, 1, SPLIT>(a, stream) : launch8<64, false, 1, SPLIT>(a, stream);
+}
+
+// Keys per split: the split count spread evenly, rounded up to whole key tiles
+// (the layout fa_fwd_split_workspace_bytes sizes).
+int64_t split_chunk8(int64_t Tk, int64_t n_split) {
+    const int64_t per = (Tk + n_split - 1) / n_split;
+    return (per + kBN - 1) / kBN * kBN;
 }
 
 fa_status run_fwd8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                    int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale, float q_descale,
-                   float k_descale, float v_descale, hipStream_t stream) {
+                   float k_descale, float v_descale, int64_t n_split, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     if (causal && Tq > Tk) return FA_ERR_SHAPE;
+    if (n_split < 1) return FA_ERR_ARG;
     if (!std::isfinite(scale)) return FA_ERR_SCALE;
     for (float ds : {q_descale, k_descale, v_descale})
         if (!std::isfinite(ds) || !(ds > 0.0f)) return FA_ERR_SCALE;
     const double cd = static_cast<double>(scale) * q_descale * k_descale * kLog2e;
     if (!std::isfinite(static_cast<float>(cd))) return FA_ERR_SCALE;
     const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
-    if ((addr(q) | addr(k) | addr(v) | addr(o)) & 15u) return FA_ERR_ALIGN;
+    if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(workspace)) & 15u) return FA_ERR_ALIGN;
     if (addr(lse) & 3u) return FA_ERR_ALIGN;
 
     // Grouped heads whose rows all see the same keys run as one problem per
@@ -522,17 +572,29 @@ fa_status run_fwd8(const void* q, const void* k, const void* v, void* o, float* 
     // element) must fit in 32-bit byte offsets, and so must the FP8 K/V rows.
     if ((Tq + 2 * bm) * 2 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
     if ((Tk + 2 * bm) * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
+    if (rows > kMax / (4 * (d + 1))) return FA_ERR_OVERFLOW;   // split workspace
+    const int64_t chunk = split_chunk8(Tk, n_split);
+    const int64_t n_eff = (Tk + chunk - 1) / chunk;   // splits that hold at least one key
     const int64_t n_qt = (Tq + bm - 1) / bm;
-    if (BH > INT32_MAX / n_qt) return FA_ERR_OVERFLOW;
+    if (BH > INT32_MAX / (n_qt * n_eff)) return FA_ERR_OVERFLOW;
+    if (n_eff > 1 && rows > static_cast<int64_t>(INT32_MAX) * (256 / (d / 4))) return FA_ERR_OVERFLOW;   // combine grid
+    // The fp32 partial rows of one head (4 bytes an element) must fit in 32-bit byte offsets too.
+    if (n_eff > 1 && (Tq + 2 * bm) * 4 * d > static_cast<int64_t>(UINT32_MAX)) return FA_ERR_OVERFLOW;
 
     const size_t q_bytes = static_cast<size_t>(rows) * static_cast<size_t>(d);
     const size_t o_bytes = 2u * q_bytes;
     const size_t kv_bytes = static_cast<size_t>(kv_rows) * static_cast<size_t>(d);
     const size_t lse_bytes = static_cast<size_t>(rows) * 4u;
     const struct { const void* p; size_t n; } ins[3] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
-    for (const auto& in : ins)
+    const size_t ws_need = n_eff > 1 ? static_cast<size_t>(n_eff) * static_cast<size_t>(rows) * (d + 1) * 4u : 0;
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
+    for (const auto& in : ins) {
         if (overlaps(o, o_bytes, in.p, in.n) || overlaps(lse, lse_bytes, in.p, in.n)) return FA_ERR_ARG;
+        if (ws_need && overlaps(workspace, ws_need, in.p, in.n)) return FA_ERR_ARG;
+    }
     if (overlaps(o, o_bytes, lse, lse_bytes)) return FA_ERR_ARG;
+    if (ws_need && (overlaps(workspace, ws_need, o, o_bytes) || overlaps(workspace, ws_need, lse, lse_bytes)))
+        return FA_ERR_ARG;
 
     Fwd8Args a;
     a.q = static_cast<const uint8_t*>(q);
@@ -540,21 +602,27 @@ fa_status run_fwd8(const void* q, const void* k, const void* v, void* o, float* 
     a.v = static_cast<const uint8_t*>(v);
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
+    a.op = static_cast<float*>(workspace);
+    a.lp = ws_need ? static_cast<float*>(workspace) + static_cast<size_t>(n_eff) * rows * d : nullptr;
+    a.rows = rows;
     a.tq = static_cast<int>(Tq);
     a.tk = static_cast<int>(Tk);
     a.n_qt = static_cast<int>(n_qt);
-    a.total = static_cast<int>(BH * n_qt);
+    a.total = static_cast<int>(BH * n_qt * n_eff);
     a.hq = static_cast<int>(Hq);
     a.group = static_cast<int>(Hq / Hkv);
+    a.chunk = static_cast<int>(chunk);
+    a.n_split = static_cast<int>(n_eff);
     a.c = static_cast<float>(cd);
     a.vscale = v_descale;
 
     hipError_t err;
-    if (d == 128) {
-        if (ng == 2) err = causal ? launch8<128, true, 2>(a, stream) : launch8<128, false, 2>(a, stream);
-        else err = causal ? launch8<128, true, 1>(a, stream) : launch8<128, false, 1>(a, stream);
+    if (n_eff == 1) {
+        err = launch8_d<false>(a, d, causal, ng, stream);
     } else {
-        err = causal ? launch8<64, true, 1>(a, stream) : launch8<64, false, 1>(a, stream);
+        err = launch8_d<true>(a, d, causal, ng, stream);
+        if (err == hipSuccess)
+            err = fa_internal::launch_split_combine(a.op, a.lp, a.o, lse, rows, a.n_split, static_cast<int>(d), stream);
     }
     if (err != hipSuccess) {
         fa_internal::record_hip_error(err);
@@ -569,5 +637,14 @@ fa_status run_fwd8(const void* q, const void* k, const void* v, void* o, float* 
 extern "C" fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                 int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale,
                                 float q_descale, float k_descale, float v_descale, hipStream_t stream) {
-    return run_fwd8(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, q_descale, k_descale, v_descale, stream);
+    return run_fwd8(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, q_descale, k_descale, v_descale, 1, nullptr,
+                    0, stream);
+}
+
+extern "C" fa_status fa_fwd_fp8_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                      int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal,
+                                      float scale, float q_descale, float k_descale, float v_descale, int64_t n_split,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return run_fwd8(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, q_descale, k_descale, v_descale, n_split,
+                    workspace, workspace_bytes, stream);
 }

@@ -101,6 +101,8 @@ WORKLOADS = [
              seed=6, sampled_rows=True, hkv=8),
     Workload("decode", "Llama-3.1-8B GQA decode B=8 Hq=32 Hkv=8 Tq=1 Tk=32768 d=128, split keys", 8, 32, 1, 128,
              True, seed=7, hkv=8, tk=32768, n_split=None),
+    Workload("decodefp8", "Llama-3.1-8B GQA decode B=8 Hq=32 Hkv=8 Tq=1 Tk=32768 d=128, split keys, FP8 E4M3 inputs",
+             8, 32, 1, 128, True, seed=7, hkv=8, tk=32768, n_split=None, fp8=True),
     # The c4 shape and draw with FP8 E4M3 inputs (per-tensor descale factors).
     Workload("c4fp8", "Llama-3.1-8B-shaped causal prefill B=1 H=32 T=8192 d=128, FP8 E4M3 inputs", 1, 32, 8192,
              128, True, seed=4, sampled_rows=True, fp8=True),

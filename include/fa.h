@@ -187,6 +187,31 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v,
                      hipStream_t stream);
 
 /*
+ * fa_fwd_fp8_split -- fa_fwd_fp8 with the keys split across workgroups.
+ *
+ * Flash-Decoding ("FlashAttention and Fused Kernels: Attention Without the
+ * n x n Matrix", Step 4) over FP8 E4M3 inputs: the keys are cut into n_split
+ * chunks exactly as for fa_fwd_split, each chunk's workgroups write their
+ * normalised fp32 output and log-sum-exp into the workspace, and the same
+ * log-sum-exp combine merges them into o and lse.  A decode step against an
+ * E4M3 cache reads half the bytes of a bf16 one.
+ *
+ * Arguments as fa_fwd_fp8, plus n_split, workspace and workspace_bytes as
+ * fa_fwd_split; the workspace layout and size are those of fa_fwd_split
+ * (fa_fwd_split_workspace_bytes gives the size, fa_fwd_split_count advice
+ * on n_split).  n_split = 1, or any n_split that leaves one chunk, is
+ * fa_fwd_fp8 and uses no workspace.  Errors as fa_fwd_fp8, plus FA_ERR_NULL
+ * for a missing workspace and FA_ERR_ARG for n_split < 1, a workspace that is
+ * too small, or overlaps.  The workspace is overwritten on every call; calls
+ * that share it must not run concurrently.
+ */
+fa_status fa_fwd_fp8_split(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                           int causal, float scale, float q_descale, float k_descale, float v_descale,
+                           int64_t n_split, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_bwd -- gradients of the exact attention forward, enqueued on `stream`.
  *
  * The backward that keeps only O and the per-row log-sum-exp from the forward

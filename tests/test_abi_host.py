@@ -246,3 +246,25 @@ def test_fp8_python_wrapper_rejects_bf16_and_cpu():
     y = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.fwd_fp8(y, y, y, True)                  # not E4M3 bytes
+
+
+def scall(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, Hq=1, Hkv=1, Tq=1, Tk=1024, d=128, causal=1, scale=0.125,
+          qd=0.01, kd=0.02, vd=0.03, n_split=4, ws=10 * A, ws_bytes=1 << 20):
+    return _lib.fa_fwd_fp8_split_raw(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, qd, kd, vd, n_split, ws,
+                                     ws_bytes, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_split=0), _lib.FA_ERR_ARG), (dict(n_split=-3), _lib.FA_ERR_ARG), (dict(ws=0), _lib.FA_ERR_NULL),
+    (dict(ws_bytes=4 * 129 * 4 - 1), _lib.FA_ERR_ARG), (dict(ws=10 * A + 8), _lib.FA_ERR_ALIGN),
+    (dict(ws=A), _lib.FA_ERR_ARG), (dict(ws=4 * A), _lib.FA_ERR_ARG), (dict(vd=0.0), _lib.FA_ERR_SCALE),
+    (dict(d=96), _lib.FA_ERR_HEAD_DIM), (dict(Tq=2, Tk=1), _lib.FA_ERR_SHAPE), (dict(q=0), _lib.FA_ERR_NULL),
+])
+def test_fp8_split_rejects(lib, kw, code):
+    assert scall(**kw) == code
+
+
+def test_fp8_split_workspace_matches_the_bf16_split(lib):
+    # 4 splits of 1024 keys for one row need 4 * (128 + 1) floats (the size the
+    # rejection cases above are measured against)
+    assert _lib.split_workspace_bytes(1, 1, 1, 1024, 128, 4) == 4 * 129 * 4

@@ -334,3 +334,48 @@ def test_side_stream_and_preallocated_outputs(fa):
     o_ref, lse_ref = fa.fwd_fp8(q, k, v, False, None, ds)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, lse_ref)
+
+
+# Split keys (fa_fwd_fp8_split): decode over a 32K cache with grouped heads at
+# several split counts (None: the library's advice), causal Tq < Tk, unmasked
+# grouped heads, causal splits that lie past some rows' diagonal (those rows
+# see no key of the split), and more splits than key tiles.
+SPLITS = [((8, 32, 8, 1, 32768, 128, True), (1, 4, 8, 16, None)),
+          ((1, 2, 2, 130, 700, 128, True), (3,)),
+          ((2, 4, 2, 200, 1000, 64, False), (2, 5)),
+          ((1, 2, 2, 300, 300, 128, True), (8,)),
+          ((1, 1, 1, 5, 100, 64, True), (64,))]
+
+
+@pytest.mark.parametrize("case,splits", SPLITS, ids=lambda c: "x".join(map(str, c)))
+def test_split_keys(fa, case, splits):
+    import torch
+    B, Hq, Hkv, Tq, Tk, d, causal = case
+    q8, k8, v8, ds = draw8((B, Hq, Tq, d), (B, Hkv, Tk, d), seed=5000 + Tk + d)
+    scale = np.float32(1.0 / math.sqrt(d))
+    q, k, v = to_dev8(q8), to_dev8(k8), to_dev8(v8)
+    for n in splits:
+        say(f"case fp8 split {case} n_split={n}")
+        o, lse = fa.fwd_fp8(q, k, v, causal, float(scale), ds, n_split=n)
+        torch.cuda.synchronize()
+        o64 = oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16))
+        check8(o64, lse.cpu().numpy().astype(np.float64), q8, k8, v8, ds, causal, scale, all_rows(q8),
+               f"fp8 split {case} n={n}")
+
+
+def test_split_workspace_reuse_and_stream(fa):
+    """One preallocated workspace, two calls of different sizes on a side stream."""
+    import torch
+    s = torch.cuda.Stream()
+    ws = torch.empty(fa.split_workspace_bytes(4, 8, 1, 8192, 128, 8), dtype=torch.uint8, device="cuda:0")
+    for Tk in (8192, 3000):
+        q8, k8, v8, ds = draw8((4, 8, 1, 128), (4, 2, Tk, 128), seed=Tk)
+        q, k, v = to_dev8(q8), to_dev8(k8), to_dev8(v8)
+        o = torch.empty((4, 8, 1, 128), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((4, 8, 1), device="cuda:0")
+        with torch.cuda.stream(s):
+            fa.fwd_fp8_out(q, k, v, o, lse, True, None, ds, n_split=8, workspace=ws)
+        s.synchronize()
+        o64 = oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16))
+        check8(o64, lse.cpu().numpy().astype(np.float64), q8, k8, v8, ds, True, np.float32(1 / math.sqrt(128)),
+               all_rows(q8), f"fp8 split workspace Tk={Tk}")

@@ -111,7 +111,7 @@ def _fp8_kernels(asm):
 
 def test_fp8_variants_use_the_fp8_matrix_cores(asm_fp8):
     kernels = dict(_fp8_kernels(asm_fp8))
-    assert len(kernels) == 6, list(kernels)   # (d=128 x causal x wave groups) + (d=64 x causal)
+    assert len(kernels) == 12, list(kernels)   # ((d=128 x causal x wave groups) + (d=64 x causal)) x split
     for name, body in kernels.items():
         ops = [l.split()[0] for l in body]
         assert "v_mfma_f32_32x32x64_f8f6f4" in ops, name
