@@ -639,6 +639,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     // lse, so they run as group * Tq query rows of that head, and each K/V
     // tile is loaded once for the whole group.
     if (Hq != Hkv && (!causal || Tq == 1)) {
+        if (Tq > INT32_MAX / (Hq / Hkv)) return FA_ERR_OVERFLOW;   // folded rows are 32-bit indices
         Tq *= Hq / Hkv;
         Hq = Hkv;
         causal = 0;   // a single query row per head sees every key either way
@@ -774,12 +775,14 @@ extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_
                                       int causal) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tq < 1 || Tk < 1 || (d != 64 && d != 128)) return 1;
     if (Hq != Hkv && (!causal || Tq == 1)) {   // folded as in the forward itself
+        if (Tq > INT32_MAX / (Hq / Hkv)) return 1;   // the forward rejects this shape
         Tq *= Hq / Hkv;
         Hq = Hkv;
         causal = 0;
     }
     const int64_t ng = d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1;
     const int64_t slots = 256 * (ng == 2 ? 1 : 2);            // CUs x resident workgroups per CU
+    if (B >= slots || Hq >= slots) return 1;                   // a full round already (and no overflow below)
     const int64_t wgs = B * Hq * ((Tq + 128 * ng - 1) / (128 * ng));
     if (wgs >= slots) return 1;
     // About one round of workgroups: a decode sweep on MI355X (64 query

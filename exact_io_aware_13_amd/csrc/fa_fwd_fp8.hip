@@ -554,6 +554,7 @@ fa_status run_fwd8(const void* q, const void* k, const void* v, void* o, float* 
     // Grouped heads whose rows all see the same keys run as one problem per
     // key/value head (the group's query rows are contiguous), as for bf16.
     if (Hq != Hkv && (!causal || Tq == 1)) {
+        if (Tq > INT32_MAX / (Hq / Hkv)) return FA_ERR_OVERFLOW;   // folded rows are 32-bit indices
         Tq *= Hq / Hkv;
         Hq = Hkv;
         causal = 0;

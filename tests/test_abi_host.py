@@ -166,6 +166,18 @@ def test_split_workspace_bytes(lib):
     assert _lib.split_workspace_bytes(0, 1, 1, 1000, 64, 2) == 0
 
 
+def test_grouped_fold_overflow(lib):
+    # Grouped heads without the mask fold the group into one head's rows; a row
+    # count past 32 bits is rejected before the fold can overflow.
+    assert call_gqa(Hq=1 << 40, Hkv=1, T=1 << 30, causal=0) == _lib.FA_ERR_OVERFLOW
+    assert call_gqa(Hq=4, Hkv=1, T=(1 << 30) + 1, causal=0) == _lib.FA_ERR_OVERFLOW
+    assert call_split(Hq=1 << 62, Hkv=1, Tq=4, Tk=64, causal=0, n_split=1) == _lib.FA_ERR_OVERFLOW
+    assert fcall(Hq=1 << 40, Hkv=1, Tq=1 << 30, Tk=1 << 30, causal=0) == _lib.FA_ERR_OVERFLOW
+    assert _lib.split_count(1, 1 << 62, 1, 4, 1 << 20, 128, False) == 1
+    assert _lib.split_count(1 << 62, 1 << 62, 1 << 62, 1, 1 << 20, 128, True) == 1
+    assert lib.fa_hip_error_string() == b""
+
+
 def test_split_count_advice(lib):
     assert _lib.split_count(1, 32, 32, 1, 32768, 128, True) > 1       # decode: one row per head
     assert _lib.split_count(1, 32, 8, 8192, 8192, 128, True) == 1     # prefill fills the GPU
