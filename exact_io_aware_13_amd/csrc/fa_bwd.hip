@@ -747,6 +747,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     if (causal && Tq > Tk) return FA_ERR_SHAPE;
     if (!std::isfinite(scale)) return FA_ERR_SCALE;
+    // The kernels take scale * log2(e) in fp32, which must stay finite.
+    if (!std::isfinite(static_cast<float>(static_cast<double>(scale) * kLog2e))) return FA_ERR_SCALE;
     const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
     if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(dout) | addr(dq) | addr(dk) | addr(dv) | addr(workspace)) & 15u)
         return FA_ERR_ALIGN;

@@ -630,6 +630,9 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (causal && Tq > Tk) return FA_ERR_SHAPE;
     if (n_split < 1) return FA_ERR_ARG;
     if (!std::isfinite(scale)) return FA_ERR_SCALE;
+    // The kernels take the exponent factor scale * log2(e) in fp32; past
+    // ~2.4e38 it would be infinite and a zero score would give 0 * inf = NaN.
+    if (!std::isfinite(static_cast<float>(static_cast<double>(scale) * kLog2e))) return FA_ERR_SCALE;
     const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
     if ((addr(q) | addr(k) | addr(v) | addr(o) | addr(workspace)) & 15u) return FA_ERR_ALIGN;
 
@@ -806,7 +809,7 @@ extern "C" const char* fa_status_string(fa_status status) {
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "sizes must be >= 1, Hq a multiple of Hkv, and Tq <= Tk when causal";
         case FA_ERR_HEAD_DIM: return "head size d must be 64 or 128";
-        case FA_ERR_SCALE: return "scale must be finite";
+        case FA_ERR_SCALE: return "scale (and scale * log2(e) in fp32; FP8: the descales, > 0) must be finite";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case FA_ERR_OVERFLOW: return "sizes overflow the supported index range";
         case FA_ERR_HIP: return "HIP kernel launch failed";

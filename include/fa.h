@@ -38,7 +38,8 @@ typedef enum {
     FA_ERR_SHAPE = 2,     /* a size < 1, Hq not a multiple of Hkv, or causal with
                              Tq > Tk                                             */
     FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
-    FA_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
+    FA_ERR_SCALE = 4,     /* scale is NaN or infinite, or scale * log2(e)
+                             overflows fp32 (|scale| > ~2.36e38)                */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte   */
     FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid,
                              or one head (T*d*2 bytes plus 2 row tiles) >= 4 GiB */
@@ -59,7 +60,8 @@ typedef enum {
  * B, H, T : batch, heads, sequence length (queries and keys alike), >= 1.
  * d       : head size, 64 or 128.
  * causal  : 1 = key j visible to query i iff j <= i; 0 = every key visible.
- * scale   : multiplies q.k; any finite value (callers usually pass
+ * scale   : multiplies q.k; any finite value with |scale| <= ~2.36e38, so
+ *           that scale * log2(e) is finite in fp32 (callers usually pass
  *           1/sqrt(d)); 0 gives uniform weights.
  * stream  : HIP stream to enqueue on; NULL means the default stream.
  *

@@ -77,7 +77,7 @@ def test_bad_head_dim(lib, d):
     assert call(d=d) == _lib.FA_ERR_HEAD_DIM
 
 
-@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf, 3e38, -3e38])
 def test_bad_scale(lib, scale):
     assert call(scale=scale) == _lib.FA_ERR_SCALE
 
@@ -202,7 +202,7 @@ def test_bwd_null_pointer(lib, which):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), _lib.FA_ERR_SHAPE), (dict(Tq=0), _lib.FA_ERR_SHAPE), (dict(Hq=3, Hkv=2), _lib.FA_ERR_SHAPE),
     (dict(Tq=17, Tk=16), _lib.FA_ERR_SHAPE), (dict(d=96), _lib.FA_ERR_HEAD_DIM),
-    (dict(scale=math.nan), _lib.FA_ERR_SCALE), (dict(causal=2), _lib.FA_ERR_ARG),
+    (dict(scale=math.nan), _lib.FA_ERR_SCALE), (dict(scale=-3e38), _lib.FA_ERR_SCALE), (dict(causal=2), _lib.FA_ERR_ARG),
     (dict(dq=7 * A + 8), _lib.FA_ERR_ALIGN), (dict(lse=6 * A + 2), _lib.FA_ERR_ALIGN),
     (dict(ws_bytes=16 * 8 - 1), _lib.FA_ERR_ARG), (dict(dk=2 * A), _lib.FA_ERR_ARG),
     (dict(dq=7 * A, dv=7 * A + 16), _lib.FA_ERR_ARG), (dict(ws=A + 64), _lib.FA_ERR_ARG),
