@@ -168,6 +168,15 @@ def _check_tensors(q, k, v):
         raise ValueError("q, k, v must be on the same device")
 
 
+def _check_workspace(workspace, device) -> None:
+    """A caller's workspace must be one contiguous GPU tensor on ``device`` (its bytes are passed raw)."""
+    import torch
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+
+
 def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: int | None = 1,
             workspace=None) -> None:
     """Exact attention forward into caller buffers ``o`` (bf16, like q) and ``lse`` (fp32, (B, Hq, Tq)).
@@ -204,6 +213,8 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
             need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split)
             if workspace is None and need > 0:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif workspace is not None:
+                _check_workspace(workspace, q.device)
             ws_ptr = workspace.data_ptr() if workspace is not None else 0
             ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
             st = fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -284,6 +295,8 @@ def fwd_fp8_out(q, k, v, o, lse, causal: bool, scale: float | None = None, desca
         need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif workspace is not None:
+            _check_workspace(workspace, q.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else 0
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         st = fa_fwd_fp8_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
@@ -326,6 +339,8 @@ def bwd_out(q, k, v, o, lse, do, dq, dk, dv, causal: bool, scale: float | None =
     need = bwd_workspace_bytes(B, Hq, Tq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),

@@ -280,3 +280,16 @@ def test_fp8_split_workspace_matches_the_bf16_split(lib):
     # 4 splits of 1024 keys for one row need 4 * (128 + 1) floats (the size the
     # rejection cases above are measured against)
     assert _lib.split_workspace_bytes(1, 1, 1, 1024, 128, 4) == 4 * 129 * 4
+
+
+def test_binding_rejects_bad_workspace():
+    """A caller workspace is passed as raw bytes: it must be one contiguous tensor on the inputs' device."""
+    import torch
+    ok = torch.empty(64, dtype=torch.uint8)
+    _lib._check_workspace(ok, ok.device)
+    with pytest.raises(TypeError):
+        _lib._check_workspace(bytearray(64), ok.device)
+    with pytest.raises(ValueError):
+        _lib._check_workspace(ok, torch.device("cuda", 0))
+    with pytest.raises(ValueError):
+        _lib._check_workspace(torch.empty(8, 8, dtype=torch.uint8).t(), ok.device)
