@@ -1,0 +1,52 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU rule, the metric's
+conventions, the keying of the committed traffic figures, and the CPU-baseline
+object."""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from exact_io_aware_13_amd import workloads as wl  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n, capsys):
+    assert bench.main(["--gpus", str(n)]) == 2
+    assert "one GPU only" in capsys.readouterr().err
+
+
+def test_metric_conventions_at_the_bench_workload():
+    w = wl.BY_KEY[wl.BENCH_KEY]
+    assert (w.B, w.H, w.T, w.d, w.causal) == (1, 32, 8192, 128, True)
+    # 4 B H T^2 d, halved for causal
+    assert w.flops() == 4.0 * 32 * 8192 ** 2 * 128 / 2 == 549755813888.0
+    # one read of Q, K, V and one write of O at 2 B/element, lse at 4 B/row
+    assert w.algorithmic_bytes() == 4 * 32 * 8192 * 128 * 2 + 32 * 8192 * 4 == 269484032
+
+
+def test_traffic_figure_is_keyed_to_the_kernel_source(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel\n")
+    fig = tmp_path / "t.json"
+    fig.write_text(json.dumps({"kernel_sha256_16": bench.kernel_hash(str(src)), "workload": "c4",
+                               "bytes_per_launch": 123}))
+    assert bench.measured_traffic("c4", str(fig), str(src)) == 123
+    assert bench.measured_traffic("c5", str(fig), str(src)) is None          # another workload
+    src.write_text("// kernel, edited\n")
+    assert bench.measured_traffic("c4", str(fig), str(src)) is None          # the source changed
+    assert bench.measured_traffic("c4", str(tmp_path / "missing.json"), str(src)) is None
+
+
+def test_cpu_baseline_object_on_the_small_workload():
+    w = wl.BY_KEY["c1"]
+    qb, kb, vb = wl.workload_inputs(w)
+    r = bench.cpu_baseline(w, qb, kb, vb, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["cores"] >= 1 and np.isfinite(r["value"]) and r["value"] > 0
+    assert "query rows" in r["sample"]
