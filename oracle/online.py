@@ -1,27 +1,25 @@
-"""The online-softmax recurrence, tile by tile, in float64.
+"""A model of the online-softmax recurrence in float64, one key tile at a time.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-This follows the row-local update stated on "Flash Attention, tiled: exact
-attention without the T x T HBM matrix", section "What happens when the maximum
-changes", and the same recurrence written as equations on "FlashAttention: the
-IO-aware Attention Kernel", section 3.2 (Online softmax):
+The pages describe the running state a query row carries across key/value
+tiles: the largest score seen so far, the sum of the exponentials taken
+relative to it, and the value rows weighted by those exponentials ("Flash
+Attention, tiled: exact attention without the T x T HBM matrix", sections
+"What happens when the maximum changes" and "From the example to tiled GPU
+work"; "FlashAttention: the IO-aware Attention Kernel", section 3.2).  This
+model writes that state as a summary of a SET of keys:
 
-    m' = max(m, max(s_tile))
-    r  = exp(m - m')                (taken as 0 while m is still -inf)
-    p  = exp(s_tile - m')
-    l  = r * l + sum(p)
-    o  = r * o + p^T @ V_tile
-    m  = m'
+    State(keys) = (m, l, o) with m = max score over the keys,
+                  l = sum of exp(score - m),  o = sum of exp(score - m) * v.
 
-and, after the last tile, Y = o / l.  The state (m, l, o) belongs to one query
-row, starts at (-inf, 0, 0) and is never reset between key/value tiles
-("From the example to tiled GPU work").
-
-The partial-state merge in ``combine`` is the Flash-Decoding combine of
-"FlashAttention and Fused Kernels: Attention Without the n x n Matrix", Step 4:
-each split gives a partial state and the pieces are rescaled to the larger
-maximum and added.
+Two summaries of disjoint key sets merge exactly: bring both to the larger
+maximum (multiply each l and o by exp(its m - larger m)) and add.  Folding a
+tile into a row is then "summarise the tile on its own, merge it into the
+row", and merging the summaries of key splits is the combine step of
+"FlashAttention and Fused Kernels: Attention Without the n x n Matrix", Step 4.
+The empty set is (-inf, 0, 0) and is the identity of the merge.  The row's
+output is o / l and its log-sum-exp m + ln l.
 """
 from __future__ import annotations
 
@@ -31,25 +29,42 @@ import numpy as np
 
 
 class RowState:
-    """Running (m, l, o) for one query row."""
+    """The (m, l, o) summary of the keys a query row has seen so far."""
 
     def __init__(self, d: int):
         self.m = -math.inf
         self.l = 0.0
         self.o = np.zeros(d, dtype=np.float64)
 
-    def update(self, s_tile: np.ndarray, v_tile: np.ndarray) -> None:
-        """Fold one tile of scores (len n) and its values (n x d) into the state."""
+    @classmethod
+    def of_tile(cls, s_tile: np.ndarray, v_tile: np.ndarray) -> "RowState":
+        """The summary of one tile alone: its own maximum, sum and weighted values."""
         s_tile = np.asarray(s_tile, dtype=np.float64)
         v_tile = np.asarray(v_tile, dtype=np.float64)
-        if s_tile.size == 0:
+        st = cls(v_tile.shape[1])
+        if s_tile.size:
+            st.m = float(np.max(s_tile))
+            w = np.exp(s_tile - st.m)
+            st.l = float(np.sum(w))
+            st.o = w @ v_tile
+        return st
+
+    def merge(self, other: "RowState") -> None:
+        """Absorb the summary of a disjoint key set."""
+        if other.l == 0.0:
             return
-        m_new = max(self.m, float(np.max(s_tile)))
-        r = 0.0 if self.m == -math.inf else math.exp(self.m - m_new)
-        p = np.exp(s_tile - m_new)
-        self.l = r * self.l + float(np.sum(p))
-        self.o = r * self.o + p @ v_tile
-        self.m = m_new
+        if self.l == 0.0:
+            self.m, self.l, self.o = other.m, other.l, other.o.copy()
+            return
+        top = max(self.m, other.m)
+        a, b = math.exp(self.m - top), math.exp(other.m - top)
+        self.l = a * self.l + b * other.l
+        self.o = a * self.o + b * other.o
+        self.m = top
+
+    def update(self, s_tile: np.ndarray, v_tile: np.ndarray) -> None:
+        """Fold one tile of scores (length n) and its value rows (n x d) into the row."""
+        self.merge(RowState.of_tile(s_tile, v_tile))
 
     def output(self) -> np.ndarray:
         return self.o / self.l
@@ -59,20 +74,17 @@ class RowState:
 
 
 def combine(states):
-    """Merge partial row states computed on disjoint key ranges."""
-    states = [s for s in states if s.l > 0.0]
+    """Merge the summaries of disjoint key ranges (for example, key splits) of one row."""
     out = RowState(states[0].o.shape[0])
-    m = max(s.m for s in states)
-    out.m = m
-    out.l = sum(math.exp(s.m - m) * s.l for s in states)
-    out.o = sum(math.exp(s.m - m) * s.o for s in states)
+    for s in states:
+        out.merge(s)
     return out
 
 
 def attention_online_f64(q, k, v, causal: bool, scale: float, block: int):
     """Tiled online-softmax attention over (B, H, T, d) float64 arrays.
 
-    Keys are visited in tiles of ``block``; each row keeps its own state.
+    Keys are visited in tiles of ``block``; each row keeps its own summary.
     Returns ``(o, lse)`` like the plain oracle.
     """
     q = np.asarray(q, dtype=np.float64)
