@@ -505,9 +505,6 @@ __global__ __launch_bounds__(512) void fa_bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ kernel.  LDS per slot: K tile, V tile.
 // Operand reads the dQ kernel keeps in flight ahead of the MFMAs (3-6 measured alike).
-#ifndef FB_DQ_AHEAD
-#define FB_DQ_AHEAD 4
-#endif
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ DO,
@@ -614,7 +611,7 @@ __device__ __forceinline__ void dq_block(const uint16_t* __restrict__ Q, const u
                 if (i & 1) dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], df[st], dp[kb], 0, 0, 0);
                 else s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[st], s[kb], 0, 0, 0);
             }
-            constexpr int kAhead = FB_DQ_AHEAD < N ? FB_DQ_AHEAD : N;
+            constexpr int kAhead = 4 < N ? 4 : N;   // operand reads in flight
             __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
             for (int i = 0; i < N - kAhead; ++i) {
@@ -665,7 +662,7 @@ __device__ __forceinline__ void dq_block(const uint16_t* __restrict__ Q, const u
                 const bf16x8 sb = as_bf16x8(dsp[kb][h8], dsp[kb][h8 + 1], dsp[kb][h8 + 2], dsp[kb][h8 + 3]);
                 dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], sb, dqa[db], 0, 0, 0);
             }
-            constexpr int kAhead = FB_DQ_AHEAD < N ? FB_DQ_AHEAD : N;
+            constexpr int kAhead = 4 < N ? 4 : N;   // operand reads in flight
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 #pragma unroll
             for (int i = 0; i < N - kAhead; ++i) {

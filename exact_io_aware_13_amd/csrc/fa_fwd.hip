@@ -86,12 +86,9 @@ constexpr double kLog2e = 1.4426950408889634;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: rescale when the max grows by > 2^8
 constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 raw buffer descriptor word 3
-#ifndef FA_MATRIX_PRIO
-#define FA_MATRIX_PRIO 1
-#endif
-#ifndef FA_SPECULATE
-#define FA_SPECULATE 1
-#endif
+constexpr uint32_t kNaN32 = 0x7FC00000u;         // quiet NaN, fp32 bits
+constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;       // two quiet NaNs, bf16 bits
+constexpr float kMaxRef = 8388608.0f;             // 2^23: largest |reference| (log2 units) with an accurate result
 
 
 // Tile geometry for head size D and NG wave groups per workgroup (4 waves of
@@ -109,6 +106,13 @@ struct Geo {
     static constexpr int kDBlocks = D / 32;           // 32-row blocks of O^T
     static constexpr int kLdsBytes = 4 * kTileBytes;  // K slot 0, K slot 1, V slot 0, V slot 1
 };
+
+// Waves per SIMD (and so the register budget: 512 / waves): NG = 2 is one
+// 8-wave workgroup per CU whose wave groups alternate phases, two waves per
+// SIMD; NG = 1 is independent 4-wave workgroups, two per CU at d = 128 and
+// three at d = 64, whose smaller tiles leave the registers for a third wave.
+template <int D, int NG>
+constexpr int kWavesPerSimd = NG == 1 && D == 64 ? 3 : 2;
 
 // XOR swizzle of the 16-byte chunk index within a tile row.  D = 128 (16
 // chunks): the two 2-bit fields of row % 16 swapped; D = 64 (8 chunks): a
@@ -240,7 +244,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     // is tail-bound: when every XCD owns whole heads, its heads are walked
     // query-tile-major, so the heaviest tiles of all of them go first.  Longer
     // grids keep the head-major order, which keeps one head's K/V in L2.
-    constexpr int kRoundSlots = 256 * (NG == 2 ? 1 : 2);   // CUs x workgroups per CU
+    constexpr int kRoundSlots = 256 * (NG == 2 ? 1 : kWavesPerSimd<D, NG>);   // CUs x workgroups per CU
     if (CAUSAL && a.n_split == 1 && r8 == 0 && q8 % n_qt == 0 && total <= 8 * kRoundSlots) {
         const int hx = q8 / n_qt;                 // heads per XCD
         bh = xcd * hx + xslot % hx;
@@ -337,10 +341,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     // the MFMA that consumes them.
     auto qk = [&] __device__ (FA_LDS const char* ks, f32x16 (&s)[2]) {
         constexpr int N = 2 * G::kDSteps;
-#ifndef FA_QK_AHEAD
-#define FA_QK_AHEAD 4
-#endif
-        constexpr int kQkAhead = FA_QK_AHEAD;
+        constexpr int kQkAhead = 4;   // K operand reads in flight ahead of their product
         bf16x8 a[N];
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -404,7 +405,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         constexpr int P = decltype(parity)::value;
         // Issue priority for the matrix phase: otherwise the older waves' softmax
         // work wins the SIMD's arbitration and starves the other group's MFMAs.
-        __builtin_amdgcn_s_setprio(FA_MATRIX_PRIO);
+        __builtin_amdgcn_s_setprio(1);
         const bool do_pv = j >= 0 && j < n_w;
         const bool do_qk = j + 1 < n_w;
         if (do_pv) pv(vslot[P], pk);
@@ -428,7 +429,6 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
                     sc[kb][i] = vis ? sc[kb][i] : -INFINITY;
                 }
         }
-        if (!FA_SPECULATE) maybe_rescale<D>(st, tile_max(sc) * c);
         // Weights against the current reference.  With speculation the tile max
         // is only taken when some weight may exceed 2^8, detected by the lane's
         // tile sum exceeding 2^8 (every weight is <= 2^8 otherwise).  Before the
@@ -447,7 +447,7 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             ts = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
         };
         weights();
-        if (FA_SPECULATE && __any(!(ts <= 256.0f))) {
+        if (__any(!(ts <= 256.0f))) {
             maybe_rescale<D>(st, tile_max(sc) * c);
             weights();
         }
@@ -510,10 +510,18 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 
     // Epilogue: O = o / l, lse = ln2 * (m + log2 l).  A row that saw no key
     // (possible only for one split of a split problem) gets O = 0, lse = -inf.
+    // The weights are exp2(fma(s, c, -m)): exact up to a common factor 2^e,
+    // where e is the rounding error of the reference m, at most half an ulp of
+    // m.  That factor cancels in O and lse, and stays within 2^(+-1/4) while
+    // |m| < 2^23.  A row whose largest scaled score reaches 2^23 in magnitude
+    // (or leaves fp32) has no accurate result and gets NaN, written as a bit
+    // pattern (the build assumes no NaN arithmetic).  m = -FLT_MAX means the
+    // row saw no key.
     const float l32 = xhalf_sum(st.l32);
     const float l16 = xhalf_sum(st.l16);
+    const bool in_range = fabsf(st.m) < kMaxRef || st.m == -3.402823466e38f;
     const float inv = l16 > 0.0f ? 1.0f / l16 : 0.0f;
-    const float lse_row = kLn2 * (st.m + __builtin_amdgcn_logf(l32));
+    const uint32_t lse_bits = in_range ? as_u32(kLn2 * (st.m + __builtin_amdgcn_logf(l32))) : kNaN32;
     if constexpr (!SPLIT) {
         if (n_w == 0) return;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + qbase, q_bytes);   // rows past Tq are dropped
@@ -523,13 +531,13 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 wv;
-                wv.x = pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv);
-                wv.y = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
+                wv.x = in_range ? pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv) : kNaN16x2;
+                wv.y = in_range ? pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv) : kNaN16x2;
                 __builtin_amdgcn_raw_buffer_store_b64(wv, ro, orow + 2 * (b * 32 + 8 * g + 4 * half), 0, 0);
             }
         if (half == 0) {
             const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)bh * Tq, (uint32_t)Tq * 4u);
-            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(lse_bits, rl, (uint32_t)qrow * 4u, 0, 0);
         }
     } else {
         // Every row of the split is written, also those that saw no key.
@@ -542,19 +550,19 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
             for (int g = 0; g < 4; ++g) {
                 u32x4 wv = {as_u32(st.o[b][4 * g + 0] * inv), as_u32(st.o[b][4 * g + 1] * inv),
                             as_u32(st.o[b][4 * g + 2] * inv), as_u32(st.o[b][4 * g + 3] * inv)};
+                if (!in_range) wv = kNaN32;
                 __builtin_amdgcn_raw_buffer_store_b128(wv, ro, orow + 4 * (b * 32 + 8 * g + 4 * half), 0, 0);
             }
         if (half == 0) {
             const __amdgpu_buffer_rsrc_t rl = make_rsrc(LP + prow, (uint32_t)Tq * 4u);
-            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(lse_bits, rl, (uint32_t)qrow * 4u, 0, 0);
         }
     }
 }
 
-// Two waves per SIMD: NG = 2 is one 8-wave workgroup per CU whose wave groups
-// alternate phases; NG = 1 is two independent 4-wave workgroups per CU.
 template <int D, bool CAUSAL, int NG, bool SPLIT>
-__global__ __launch_bounds__(256 * NG) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256 * NG)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, NG>, kWavesPerSimd<D, NG>)))
 void fa_fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[Geo<D, NG>::kLdsBytes];
     fa_fwd_block<D, CAUSAL, NG, SPLIT>(a.q, a.k, a.v, a.o, a.lse, a.op, a.lp, a, (FA_LDS char*)smem);
@@ -575,7 +583,12 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const float* __restrict
     const int t = threadIdx.x % kLanes;
     if (row >= rows) return;
     float m = -INFINITY;
-    for (int s = 0; s < n_split; ++s) m = fmaxf(m, lp[(size_t)s * rows + row]);
+    bool nan = false;   // a split that flagged its row (score outside fp32): the row is NaN
+    for (int s = 0; s < n_split; ++s) {
+        const float ls = lp[(size_t)s * rows + row];
+        nan |= (as_u32(ls) & 0x7FFFFFFFu) > 0x7F800000u;
+        m = fmaxf(m, ls);
+    }
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float l = 0.0f;
     for (int s = 0; s < n_split; ++s) {
@@ -588,10 +601,10 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const float* __restrict
     }
     const float inv = 1.0f / l;
     u32x2 wv;
-    wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    wv.x = nan ? kNaN16x2 : pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    wv.y = nan ? kNaN16x2 : pack_bf16x2(acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<u32x2*>(o + (size_t)row * D + 4 * t) = wv;
-    if (t == 0) lse[row] = m + kLn2 * __builtin_amdgcn_logf(l);
+    if (t == 0) reinterpret_cast<uint32_t*>(lse)[row] = nan ? kNaN32 : as_u32(m + kLn2 * __builtin_amdgcn_logf(l));
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -653,10 +666,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     // d = 128 and each query tile walks many key tiles (T >= 8192 causal, or
     // T >= 4096 without the mask); otherwise two independent 4-wave workgroups
     // per CU are faster.  Both shapes give bit-identical results.
-#ifndef FA_FORCE_GROUPS
-#define FA_FORCE_GROUPS 0
-#endif
-    const int ng = FA_FORCE_GROUPS ? FA_FORCE_GROUPS : (d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1);
+    const int ng = d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1;
     const int64_t bm = 128 * ng;
 
     // Sizes: every byte count must fit int64; in-kernel row and key indices are 32-bit.
@@ -784,7 +794,7 @@ extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_
         causal = 0;
     }
     const int64_t ng = d == 128 && Tq * (causal ? 1 : 2) >= 8192 ? 2 : 1;
-    const int64_t slots = 256 * (ng == 2 ? 1 : 2);            // CUs x resident workgroups per CU
+    const int64_t slots = 256 * (ng == 2 ? 1 : (d == 64 ? 3 : 2));   // CUs x resident workgroups per CU
     if (B >= slots || Hq >= slots) return 1;                   // a full round already (and no overflow below)
     const int64_t wgs = B * Hq * ((Tq + 128 * ng - 1) / (128 * ng));
     if (wgs >= slots) return 1;

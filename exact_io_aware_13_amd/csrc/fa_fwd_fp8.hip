@@ -74,6 +74,8 @@ constexpr float kWeightShift = 3.0f;       // weights are 2^3 * 2^(x - m_ref)
 constexpr float kRescaleThreshold = 8.0f;  // rescale when 2^(x - m) may exceed 2^8 (max grew by > 2^5)
 constexpr float kSpecSum = 448.0f;         // a lane's tile sum <= 448 bounds each weight by E4M3's largest
 constexpr uint32_t kBufferFlags = 0x00020000u;
+constexpr uint32_t kNaN32 = 0x7FC00000u;     // quiet NaN, fp32 bits
+constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;   // two quiet NaNs, bf16 bits
 constexpr int kOnesE4m3 = 0x38383838;      // four E4M3 ones
 
 template <int D, int NG>
@@ -454,11 +456,15 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
 
     // Epilogue: O = v_descale * o / l8, lse = ln2 * (m + log2 l32).  A row that
     // saw no key (possible only for one split of a split problem) gets O = 0,
-    // lse = -inf.
+    // lse = -inf.  A row whose largest scaled score reaches 2^23 in magnitude
+    // (log2 units) has no accurate result, as in the bf16 forward (there the
+    // reference's rounding could also push a weight past 448), and gets NaN,
+    // written as a bit pattern (the build assumes no NaN arithmetic).
     const float l32 = xhalf_sum(st.l32);
     const float l8 = st.l8[0];
+    const bool in_range = fabsf(st.m) < 8388608.0f || st.m == -3.402823466e38f;
     const float inv = l8 > 0.0f ? a.vscale / l8 : 0.0f;
-    const float lse_row = kLn2 * (st.m + __builtin_amdgcn_logf(l32));
+    const uint32_t lse_bits = in_range ? as_u32(kLn2 * (st.m + __builtin_amdgcn_logf(l32))) : kNaN32;
     if constexpr (SPLIT) {
         // Every row of the split is written, also those that saw no key.
         const size_t prow = (size_t)split * (size_t)a.rows + (size_t)bh * Tq;
@@ -470,11 +476,12 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
             for (int g = 0; g < 4; ++g) {
                 u32x4 wv = {as_u32(st.o[b][4 * g + 0] * inv), as_u32(st.o[b][4 * g + 1] * inv),
                             as_u32(st.o[b][4 * g + 2] * inv), as_u32(st.o[b][4 * g + 3] * inv)};
+                if (!in_range) wv = kNaN32;
                 __builtin_amdgcn_raw_buffer_store_b128(wv, rp, prow_b + 4 * (b * 32 + 8 * g + 4 * half), 0, 0);
             }
         if (half == 0) {
             const __amdgpu_buffer_rsrc_t rl = make_rsrc(LP + prow, (uint32_t)Tq * 4u);
-            __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(lse_bits, rl, (uint32_t)qrow * 4u, 0, 0);
         }
         return;
     }
@@ -486,13 +493,13 @@ __device__ __forceinline__ void fa_fwd8_block(const uint8_t* __restrict__ Q, con
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             u32x2 wv;
-            wv.x = pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv);
-            wv.y = pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv);
+            wv.x = in_range ? pack_bf16x2(st.o[b][4 * g + 0] * inv, st.o[b][4 * g + 1] * inv) : kNaN16x2;
+            wv.y = in_range ? pack_bf16x2(st.o[b][4 * g + 2] * inv, st.o[b][4 * g + 3] * inv) : kNaN16x2;
             __builtin_amdgcn_raw_buffer_store_b64(wv, ro, orow + 2 * (b * 32 + 8 * g + 4 * half), 0, 0);
         }
     if (half == 0) {
         const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + (size_t)bh * Tq, (uint32_t)Tq * 4u);
-        __builtin_amdgcn_raw_buffer_store_b32(as_u32(lse_row), rl, (uint32_t)qrow * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(lse_bits, rl, (uint32_t)qrow * 4u, 0, 0);
     }
 }
 

@@ -62,7 +62,11 @@ typedef enum {
  * causal  : 1 = key j visible to query i iff j <= i; 0 = every key visible.
  * scale   : multiplies q.k; any finite value with |scale| <= ~2.36e38, so
  *           that scale * log2(e) is finite in fp32 (callers usually pass
- *           1/sqrt(d)); 0 gives uniform weights.
+ *           1/sqrt(d)); 0 gives uniform weights.  The exponent arithmetic
+ *           is fp32: a row whose largest visible scaled score, in log2 units
+ *           |scale * q.k * log2(e)|, reaches 2^23 (~8.4e6) has no accurate
+ *           result (far past where the softmax is a hard maximum), and its o
+ *           and lse are written as NaN, never as a plausible-looking value.
  * stream  : HIP stream to enqueue on; NULL means the default stream.
  *
  * Ownership: the caller allocates and owns every buffer.  The library
@@ -122,6 +126,10 @@ fa_status fa_fwd_gqa(const void* q, const void* k, const void* v,
  * Grouped heads with no mask (or one query row per head) run as one problem
  * per key/value head with Hq / Hkv * Tq query rows, so every key/value tile is
  * read once per group rather than once per query head.
+ *
+ * A row is written as NaN (o and lse) as for fa_fwd, and also when the
+ * largest visible scaled score of any one of its chunks reaches 2^23 in log2
+ * units: each chunk's partial result is held to the same fp32 range.
  *
  * The workspace is overwritten on every call; calls that share it must not
  * run concurrently.  The two kernels are enqueued in order on `stream`.

@@ -91,7 +91,9 @@ def test_queries_and_keys_differ(fa, B, Hq, Hkv, Tq, Tk, d, causal):
 
 SPLIT = [(1, 8, 2, 1, 3000, 128, True, 4), (2, 8, 2, 7, 3000, 64, False, 3), (1, 4, 1, 130, 2049, 128, True, 5),
          (1, 4, 4, 1000, 1000, 64, True, 4), (1, 2, 2, 64, 200, 128, False, 16), (1, 2, 1, 3, 70, 64, True, 2),
-         (1, 32, 8, 1, 32768, 128, True, None), (4, 32, 8, 1, 4096, 128, False, None)]
+         (1, 32, 8, 1, 32768, 128, True, None), (4, 32, 8, 1, 4096, 128, False, None),
+         # long rows at d = 128 take the 8-wave workgroup with split keys
+         (1, 1, 1, 8200, 8200, 128, True, None), (1, 2, 2, 4100, 4100, 128, False, 3)]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,n_split", SPLIT, ids=lambda x: str(x))

@@ -300,3 +300,51 @@ def test_side_stream_and_preallocated_outputs(fa):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, False, 1.0 / math.sqrt(128))
     check(bf16_to_f64(o), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref, "side stream")
+
+
+# ---------------------------------------------------------------------------
+# The fp32 range of the scaled scores
+# ---------------------------------------------------------------------------
+
+def _argmax_inputs(T, d, seed):
+    """q_i = (a_i, 0, ...), k_j = (b_j, 0, ...): every score a_i * b_j is exact in fp32."""
+    rng = np.random.default_rng(seed)
+    a = np.array([0.0, 1.0, -1.0, 0.5, 64.0, -64.0, 0.25, -32.0] * (T // 8), dtype=np.float32)
+    b = (rng.permutation(T).astype(np.float32) - T / 2) / 8.0      # distinct, exact in bf16
+    q = np.zeros((1, 1, T, d), np.float32); q[0, 0, :, 0] = a
+    k = np.zeros((1, 1, T, d), np.float32); k[0, 0, :, 0] = b
+    v = rng.standard_normal((1, 1, T, d), dtype=np.float32)
+    return a.astype(np.float64), b.astype(np.float64), *(wl.f32_to_bf16_bits(x) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("scale,n_split", [(1e3, 1), (-1e3, 1), (5e4, 1), (5e4, 2), (1e37, 1), (1e37, 2)])
+def test_huge_scales(fa, scale, n_split):
+    """Large scales.  A row whose largest scaled score (log2 units) stays below
+    2^23 must agree with the oracle, lse to fp32's relative precision since it
+    can be ~1e6; a row whose largest scaled score reaches 2^23 (or overflows
+    fp32) has no accurate fp32 result and must come back NaN in O and lse,
+    through the split combine too."""
+    import torch
+    T, d = 128, 64
+    a, b, qb, kb, vb = _argmax_inputs(T, d, seed=5)
+    sigma = float(np.float32(scale))
+    s_max = np.max(np.outer(a, b) * sigma * math.log2(math.e), axis=1)
+    over = s_max >= 2.0 ** 23
+    assert np.all((s_max >= 2.0 ** 24) | (s_max <= 2.0 ** 22)), "inputs must stay clear of the edge"
+    chunk = T // n_split      # with splits, every split of an accurate row must stay in range too
+    split_max = np.abs(np.max((np.outer(a, b) * sigma * math.log2(math.e)).reshape(T, n_split, chunk), axis=2))
+    assert np.all(split_max[~over] <= 2.0 ** 22)
+    o, lse = fa.fwd(to_dev(qb), to_dev(kb), to_dev(vb), False, sigma, n_split=n_split)
+    torch.cuda.synchronize()
+    o = bf16_to_f64(o)[0, 0]
+    lse = lse.cpu().numpy().astype(np.float64)[0, 0]
+    o_ref, lse_ref = oracle.attention_f64(qb, kb, vb, False, sigma)
+    o_ref, lse_ref = o_ref[0, 0], lse_ref[0, 0]
+    say(f"[scale {scale:g} splits {n_split}] rows out of range: {int(over.sum())} of {T}")
+    assert np.all(np.isnan(o[over])) and np.all(np.isnan(lse[over]))
+    ok = ~over
+    assert np.all(np.isfinite(o[ok])) and np.all(np.isfinite(lse[ok]))
+    assert np.abs(o[ok] - o_ref[ok]).max() <= O_MAX_ABS
+    assert np.all(np.abs(lse[ok] - lse_ref[ok]) <= LSE_MAX_ABS + 1e-6 * np.abs(lse_ref[ok]))
+    if scale > 1e4:
+        assert over.any() and ok.any()
