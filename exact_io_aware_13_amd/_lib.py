@@ -23,8 +23,10 @@ FA_ERR_ALIGN = 5
 FA_ERR_OVERFLOW = 6
 FA_ERR_HIP = 7
 FA_ERR_ARG = 8
+FA_ERR_SCRATCH = 9
+SCRATCH_BYTES = 16 << 20      # FA_SCRATCH_BYTES: the fixed scratch of fa_fwd_split_noalloc
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
             "fa_fwd_fp8", "fa_fwd_fp8_split", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
 
 _lib = None
@@ -52,6 +54,9 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_float, i64, vp, ctypes.c_size_t, vp]
         lib.fa_fwd_split.restype = ctypes.c_int
+        lib.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_float, i64, vp]
+        lib.fa_fwd_split_noalloc.restype = ctypes.c_int
         lib.fa_fwd_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
@@ -100,6 +105,14 @@ def fa_fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: in
     """Call ``fa_fwd_split`` with raw addresses; returns the fa_status code."""
     return int(load().fa_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
                                    float(scale), n_split, ws_ptr, ws_bytes, stream))
+
+
+def fa_fwd_split_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int,
+                             Hkv: int, Tq: int, Tk: int, d: int, causal: int, scale: float, n_split: int,
+                             stream: int) -> int:
+    """Call ``fa_fwd_split_noalloc`` with raw addresses; returns the fa_status code."""
+    return int(load().fa_fwd_split_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d,
+                                           int(causal), float(scale), int(n_split), stream))
 
 
 def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: int) -> int:
@@ -221,6 +234,30 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
                                   B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), int(n_split),
                                   ws_ptr, ws_bytes, stream)
         _check(st)
+
+
+def fwd_noalloc_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: int | None = None) -> None:
+    """``fwd_out`` with split keys through ``fa_fwd_split_noalloc``: no memory is
+    allocated, by the library or here; the partial results go to the library's
+    fixed per-GPU scratch (``SCRATCH_BYTES``).  Calls that overlap on one GPU
+    race on that scratch.  ``n_split=None`` asks the library for a split count."""
+    import torch
+    _check_tensors(q, k, v)
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("o must be a contiguous bf16 tensor shaped like q on q's device")
+    if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Tq) on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_split is None:
+        n_split = split_count(B, Hq, Hkv, Tq, Tk, d, causal)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_split_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), int(n_split), stream)
+    _check(st, "fa_fwd_split_noalloc")
 
 
 def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None = 1):

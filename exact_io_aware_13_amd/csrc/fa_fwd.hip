@@ -64,6 +64,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -631,10 +632,53 @@ int64_t split_chunk(int64_t Tk, int64_t n_split) {
     return (per + kBN - 1) / kBN * kBN;
 }
 
-// The general forward behind every entry point.
+// The library's fixed split-key scratch, for callers that cannot allocate
+// (fa_fwd_split_noalloc).  Each GPU holds its own copy until the process
+// ends.  Host code never passes `scratch` itself to a kernel: its device
+// address, per device, comes from hipGetSymbolAddress (fixed_scratch).
+constexpr size_t kScratchBytes = FA_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that `stream` runs on, looked
+// up once per device with that device current.
+fa_status fixed_scratch(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        fa_internal::record_hip_error(err);
+        return FA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        err = hipGetDevice(&cur);
+        if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+        void* ptr = nullptr;
+        if (err == hipSuccess) err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess || !ptr) {
+            fa_internal::record_hip_error(err != hipSuccess ? err : hipErrorInvalidSymbol);
+            return FA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+// The general forward behind every entry point.  With fixed_ws, the split
+// workspace is the library's fixed scratch instead of the caller's.
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
                   int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal, float scale, int64_t n_split,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream, bool fixed_ws = false) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
@@ -689,13 +733,24 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     const size_t kv_bytes = static_cast<size_t>(kv_rows) * static_cast<size_t>(d) * 2u;
     const size_t lse_bytes = static_cast<size_t>(rows) * 4u;
     const size_t ws_need = n_eff > 1 ? static_cast<size_t>(n_eff) * static_cast<size_t>(rows) * (d + 1) * 4u : 0;
-    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
+    if (n_eff > 1 && rows > static_cast<int64_t>(INT32_MAX) * (256 / (d / 4))) return FA_ERR_OVERFLOW;   // combine grid
     const struct { const void* p; size_t n; } ins[3] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
-    for (const auto& in : ins) {
+    for (const auto& in : ins)
         if (overlaps(o, q_bytes, in.p, in.n) || overlaps(lse, lse_bytes, in.p, in.n)) return FA_ERR_ARG;
-        if (ws_need && overlaps(workspace, ws_need, in.p, in.n)) return FA_ERR_ARG;
-    }
     if (overlaps(o, q_bytes, lse, lse_bytes)) return FA_ERR_ARG;
+    if (fixed_ws) {   // every argument is checked by now: the HIP calls start here
+        if (ws_need > kScratchBytes) return FA_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (ws_need > 0) {
+            const fa_status st = fixed_scratch(stream, &workspace);
+            if (st != FA_OK) return st;
+            workspace_bytes = kScratchBytes;
+        }
+    }
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return workspace ? FA_ERR_ARG : FA_ERR_NULL;
+    for (const auto& in : ins)
+        if (ws_need && overlaps(workspace, ws_need, in.p, in.n)) return FA_ERR_ARG;
     if (ws_need && (overlaps(workspace, ws_need, o, q_bytes) || overlaps(workspace, ws_need, lse, lse_bytes)))
         return FA_ERR_ARG;
 
@@ -722,7 +777,6 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (n_eff == 1) {
         err = d == 128 ? launch_d<128, false>(a, causal, ng, stream) : launch_d<64, false>(a, causal, ng, stream);
     } else {
-        if (rows > static_cast<int64_t>(INT32_MAX) * (256 / (d / 4))) return FA_ERR_OVERFLOW;   // combine grid
         err = d == 128 ? launch_d<128, true>(a, causal, ng, stream) : launch_d<64, true>(a, causal, ng, stream);
         if (err == hipSuccess)
             err = fa_internal::launch_split_combine(a.op, a.lp, a.o, lse, rows, a.n_split, static_cast<int>(d), stream);
@@ -813,6 +867,12 @@ extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, v
                    stream);
 }
 
+extern "C" fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                          int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, int causal,
+                                          float scale, int64_t n_split, hipStream_t stream) {
+    return run_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split, nullptr, 0, stream, true);
+}
+
 extern "C" const char* fa_status_string(fa_status status) {
     switch (status) {
         case FA_OK: return "ok";
@@ -824,6 +884,7 @@ extern "C" const char* fa_status_string(fa_status status) {
         case FA_ERR_OVERFLOW: return "sizes overflow the supported index range";
         case FA_ERR_HIP: return "HIP kernel launch failed";
         case FA_ERR_ARG: return "bad argument: causal not 0/1, n_split < 1, workspace too small, or overlapping buffers";
+        case FA_ERR_SCRATCH: return "the split keys need more scratch than the library's fixed buffer (FA_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

@@ -44,9 +44,14 @@ typedef enum {
     FA_ERR_OVERFLOW = 6,  /* sizes overflow 64-bit byte counts or the launch grid,
                              or one head (T*d*2 bytes plus 2 row tiles) >= 4 GiB */
     FA_ERR_HIP = 7,       /* the kernel launch failed; see fa_hip_error_string()  */
-    FA_ERR_ARG = 8        /* causal not 0/1, n_split < 1, workspace too small, or
+    FA_ERR_ARG = 8,       /* causal not 0/1, n_split < 1, workspace too small, or
                              overlapping buffers                                 */
+    FA_ERR_SCRATCH = 9    /* fa_fwd_split_noalloc: the split needs more than
+                             FA_SCRATCH_BYTES of scratch                         */
 } fa_status;
+
+/* Size of the library's fixed split-key scratch (fa_fwd_split_noalloc). */
+#define FA_SCRATCH_BYTES ((size_t)16 << 20)
 
 /*
  * fa_fwd -- exact attention forward, enqueued on `stream`.
@@ -141,6 +146,36 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v,
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
                        int causal, float scale, int64_t n_split,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_fwd_split_noalloc -- fa_fwd_split for callers that cannot allocate.
+ *
+ * For code that may not call hipMalloc: under HIP graph capture, inside tight
+ * serving loops, or in harnesses that forbid allocation.  It runs exactly
+ * fa_fwd_split's kernels (same results, bit for bit), but the chunks' partial
+ * results go to a fixed scratch buffer inside the library instead of a caller
+ * workspace.  The arguments are fa_fwd_split's without the workspace.
+ *
+ * Scratch: FA_SCRATCH_BYTES (16 MiB) of device memory per GPU, a static array
+ * that each GPU the library runs on holds until the process ends.  A call
+ * needs fa_fwd_split_workspace_bytes(B, Hq, Tq, Tk, d, n_split) bytes of it;
+ * a larger need returns FA_ERR_SCRATCH before any HIP call (for example,
+ * d = 128 with n_split = 8 fits 4064 query rows).  The first call on a device
+ * looks up the array's device address once (hipGetSymbolAddress); no call
+ * allocates or frees memory.  The scratch needs no clearing: every chunk
+ * writes all of its rows before the combine reads them.
+ *
+ * Every call on a GPU shares that GPU's scratch and leaves it holding its
+ * partials: calls that overlap on one GPU (several streams or host threads)
+ * race and give wrong results.  Serialise them.  The stream's device
+ * selects the scratch; the calling thread's current device is unchanged.
+ * Errors as fa_fwd_split (no workspace errors), plus FA_ERR_SCRATCH.
+ */
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v,
+                               void* o, float* lse,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                               int64_t d, int causal, float scale, int64_t n_split,
+                               hipStream_t stream);
 
 /* Workspace bytes fa_fwd_split needs for these sizes (0: none needed, or
  * invalid sizes). */

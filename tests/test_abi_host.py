@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = _lib.status_string(code)
         assert s and s != "unknown status"
     assert _lib.status_string(99) == "unknown status"
@@ -153,6 +153,35 @@ def test_split_workspace_rules(lib):
     assert call_split(ws_bytes=need - 4) == _lib.FA_ERR_ARG
     assert call_split(ws=16 * A + 4) == _lib.FA_ERR_ALIGN
     assert call_split(ws=A) == _lib.FA_ERR_ARG                               # workspace over q
+
+
+def call_noalloc(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, Hq=4, Hkv=2, Tq=4, Tk=1024, d=64, causal=1,
+                 scale=0.125, n_split=4):
+    return _lib.fa_fwd_split_noalloc_raw(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split, 0)
+
+
+def test_noalloc_validates_before_any_hip_call(lib):
+    # every argument check of fa_fwd_split, and then the scratch bound, come before any HIP call
+    assert call_noalloc(q=0) == _lib.FA_ERR_NULL
+    assert call_noalloc(Tq=2048, Tk=1024) == _lib.FA_ERR_SHAPE
+    assert call_noalloc(d=96) == _lib.FA_ERR_HEAD_DIM
+    assert call_noalloc(n_split=0) == _lib.FA_ERR_ARG
+    assert call_noalloc(scale=float("inf")) == _lib.FA_ERR_SCALE
+    assert call_noalloc(o=4 * A + 2) == _lib.FA_ERR_ALIGN
+    assert call_noalloc(o=A) == _lib.FA_ERR_ARG                             # o over q
+    assert lib.fa_hip_error_string() == b""
+
+
+def test_noalloc_rejects_splits_beyond_its_scratch(lib):
+    # 8 chunks of d = 128 rows take 8 * 129 * 4 bytes per query row: 4064 rows fit in 16 MiB, 4065 do not
+    assert _lib.SCRATCH_BYTES == 16 << 20
+    fits = _lib.split_workspace_bytes(1, 1, 4064, 8192, 128, 8)
+    assert fits <= _lib.SCRATCH_BYTES < _lib.split_workspace_bytes(1, 1, 4065, 8192, 128, 8)
+    far = {n: (i + 1) << 32 for i, n in enumerate(("q", "k", "v", "o", "lse"))}   # buffers far apart
+    assert call_noalloc(**far, Hq=1, Hkv=1, Tq=4065, Tk=8192, d=128, causal=0, n_split=8) == _lib.FA_ERR_SCRATCH
+    assert call_noalloc(**far, B=64, Hq=32, Hkv=8, Tq=1, Tk=32768, d=128, causal=1, n_split=64) == _lib.FA_ERR_SCRATCH
+    assert "scratch" in _lib.status_string(_lib.FA_ERR_SCRATCH)
+    assert lib.fa_hip_error_string() == b""
 
 
 def test_split_workspace_bytes(lib):
