@@ -272,7 +272,8 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
     const int n_w = qw0 >= Tq || w_end <= k_lo ? 0 : (w_end - k_lo + kBN - 1) / kBN;   // tiles it uses
     // Tiles from j_mask on can hold keys some row of the wave must not see
     // (past its diagonal, or past the split): at most the last two.
-    const int j_mask = CAUSAL ? min(n_w - 1, max(0, (qw0 + off + 1 - k_lo) / kBN)) : n_w - 1;
+    const int j_mask = CAUSAL ? min(n_w - 1, max(0, (qw0 + off + 1 - k_lo) / kBN))
+                              : (k_hi - k_lo) % kBN == 0 ? n_w : n_w - 1;   // a full last tile needs no mask
 
     // Per-lane byte offsets of this lane's 16-byte chunk in each tile load; the
     // wave's 1 KB blocks of a tile are contiguous in LDS.
@@ -435,6 +436,9 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         // tile sum exceeding 2^8 (every weight is <= 2^8 otherwise).  Before the
         // first rescale the reference is -FLT_MAX and the visible weights are
         // inf, which also takes the max.
+        // The first tile takes its max at once: against the initial reference
+        // every weight would be infinite and the speculation would fail.
+        if (j == 0) maybe_rescale<D>(st, tile_max(sc) * c);
         float p[32];
         float ts;
         auto weights = [&] __device__ () {
