@@ -110,17 +110,18 @@ def _row_scores(q, k, causal, scale, rows):
         yield scale * (kk @ q[b, h, i]), np.abs(kk * q[b, h, i]).max(axis=1), (b, h // g, n)
 
 
-def score_error_rows(q, k, causal: bool, scale: float, rows) -> np.ndarray:
+def score_error_rows(q, k, causal: bool, scale: float, rows, kappa: float = KAPPA_MFMA) -> np.ndarray:
     """Per selected row, a bound on how far the kernel's scores (and so its lse)
-    may move: max_j of 2 KAPPA_MFMA |scale| max_k |q_k kk_jk| plus fp32 rounding
-    of the scaled score (module docstring)."""
+    may move: max_j of 2 kappa |scale| max_k |q_k kk_jk| plus fp32 rounding
+    of the scaled score (module docstring; kappa = KAPPA_MFMA unless a caller
+    asks how much of the bound the instruction's term is)."""
     out = []
     for s, pmax, _ in _row_scores(q, k, causal, scale, rows):
-        out.append(float(np.max(2.0 * KAPPA_MFMA * abs(scale) * pmax + 4.0 * U_F32 * np.abs(s))))
+        out.append(float(np.max(2.0 * kappa * abs(scale) * pmax + 4.0 * U_F32 * np.abs(s))))
     return np.asarray(out)
 
 
-def _row_terms(q, k, v, causal, scale, rows):
+def _row_terms(q, k, v, causal, scale, rows, kappa=KAPPA_MFMA):
     """Per selected row: the exact weights w, Z, O, the visible V rows and the score bound."""
     _check4(q, k, v)
     for s, pmax, (b, hk, n) in _row_scores(q, k, causal, scale, rows):
@@ -128,22 +129,23 @@ def _row_terms(q, k, v, causal, scale, rows):
         e = np.exp(s - s.max())
         z = e.sum()
         w = e / z
-        delta = float(np.max(2.0 * KAPPA_MFMA * abs(scale) * pmax + 4.0 * U_F32 * np.abs(s)))
+        delta = float(np.max(2.0 * kappa * abs(scale) * pmax + 4.0 * U_F32 * np.abs(s)))
         yield w, z, w @ vv, vv, delta
 
 
-def pv_error_bound_rows(q, k, v, causal: bool, scale: float, rows) -> np.ndarray:
+def pv_error_bound_rows(q, k, v, causal: bool, scale: float, rows, kappa: float = KAPPA_MFMA) -> np.ndarray:
     """Per-element bound (n, d) on |O_fp8 - O| for the selected rows of the
     dequantised problem (float64 operands), from the FP8 rounding of the
     weights, the FP8 matrix instruction's summation, the fp32 accumulation and
-    the bf16 store (module docstring)."""
+    the bf16 store (module docstring).  ``kappa`` is the instruction's term,
+    KAPPA_MFMA unless a caller asks how much of the bound that term is."""
     out = []
-    for w, z, o, vv, delta in _row_terms(q, k, v, causal, scale, rows):
+    for w, z, o, vv, delta in _row_terms(q, k, v, causal, scale, rows, kappa):
         omega = np.maximum(U_FP8 * w, np.minimum(A_FP8 / z, w))
         big = omega.sum()
         dev = np.abs(vv - o)                       # (n, d)
         wv = w @ np.abs(vv)
-        acc = 2.0 * len(w) * U_F32 * wv + KAPPA_MFMA * (1.0 + U_FP8) * (wv + np.abs(o))
+        acc = 2.0 * len(w) * U_F32 * wv + kappa * (1.0 + U_FP8) * (wv + np.abs(o))
         shift = np.expm1(2.0 * delta) * (w @ dev)  # the scores' error moves the weights
         b = (omega @ dev + acc + shift) / (1.0 - big) if big < 0.5 else np.full(o.shape, np.inf)
         out.append(b + U_BF16 * (np.abs(o) + b))

@@ -9,14 +9,18 @@ tolerance is derived from that arithmetic, not taken from the bf16 forward:
   oracle (the per-element bound of ``oracle.fp8``: the weights' rounding, the
   FP8 matrix instruction's summation, fp32 accumulation, the bf16 store; 1%
   covers the exponentials it leaves out);
-* the root of the summed squared error within 1.5 times the estimate
-  ``pv_error_rms_rows`` (an expectation, not a bound: an emulation of the
-  rounding lands near 0.6 of it, and rows whose weights are nearly one-hot,
-  as in the spiky draws, make the sum of squares heavy-tailed; measured
-  0.05-0.9);
 * lse (fp32 weights) within 1e-3 plus the per-row bound on the scores' own
   error (``score_error_rows``: the matrix instruction sums the 64 products of
   a score block to within 2^-10 of the largest one).
+
+The instruction's figure 2^-10 is itself checked on this hardware by
+``test_matrix_instruction_summation_error``, and every check reports the share
+of the bound that the instruction's term takes.  The root of the summed squared
+error is reported beside the estimate ``pv_error_rms_rows`` but not asserted:
+that estimate is an expectation under uniform, independent rounding errors,
+and an emulation of the E4M3 weights shows single rows with few dominant
+weights far above it (``test_oracle_fp8.py::test_rms_estimate_is_no_bound``),
+so no fixed multiple of it bounds the error; the per-element bound does.
 
 Closed forms need less: all-equal scores give weights of exactly 8, so Q = 0
 yields the running mean of V, and V = 1 yields v_descale exactly.
@@ -81,6 +85,8 @@ def check8(o, lse, q8, k8, v8, ds, causal, scale, rows, label):
     d = q8.shape[-1]
     o_ref, lse_ref = oracle.attention_rows_f64(qf, kf, vf, causal, float(scale), rows)
     bound = ofp8.pv_error_bound_rows(qf, kf, vf, causal, float(scale), rows)
+    bound0 = ofp8.pv_error_bound_rows(qf, kf, vf, causal, float(scale), rows, kappa=0.0)
+    kappa_share = float(np.max(1.0 - bound0 / np.maximum(bound, 1e-300)))
     rms_pred = ofp8.pv_error_rms_rows(qf, kf, vf, causal, float(scale), rows)
     got = o.reshape(-1, d)[rows]
     err = np.abs(got - o_ref)
@@ -91,11 +97,11 @@ def check8(o, lse, q8, k8, v8, ds, causal, scale, rows, label):
     lse_abs = float(lse_err.max())
     rel_l2 = float(np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
     say(f"[{label}] {len(rows)} rows: O max-abs {err.max():.3e}, worst err/bound {ratio:.3f}, "
-        f"rms err / estimate {rms / max(rms_pred, 1e-30):.3f}, rel-L2 {rel_l2:.3e}, lse max-abs {lse_abs:.3e}")
+        f"rms err / estimate {rms / max(rms_pred, 1e-30):.3f}, rel-L2 {rel_l2:.3e}, lse max-abs {lse_abs:.3e}, "
+        f"largest share of an element's bound from the instruction's term {kappa_share:.3f}")
     assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse.reshape(-1)[rows]))
     bad = err > 1.01 * bound + 1e-6
     assert not np.any(bad), (label, np.argwhere(bad)[:5], err[bad][:5], bound[bad][:5])
-    assert rms <= 1.5 * rms_pred, (label, rms, rms_pred)
     assert np.all(lse_err <= lse_tol), (label, lse_abs, float(lse_tol[np.argmax(lse_err)]))
 
 
@@ -361,6 +367,72 @@ def test_split_keys(fa, case, splits):
         o64 = oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16))
         check8(o64, lse.cpu().numpy().astype(np.float64), q8, k8, v8, ds, causal, scale, all_rows(q8),
                f"fp8 split {case} n={n}")
+
+
+def test_matrix_instruction_summation_error(fa):
+    """The FP8 matrix instruction's own summation error, measured through the
+    library: with split keys, each 64-key chunk's partial output is one
+    instruction's 64-product sum (and the weight sum another's), divided in fp32
+    and left in the caller's workspace before the combine.  With whole-number
+    scores (scale = ln 2) the weights 8 * 2^-k are exact in E4M3, so a partial's
+    only errors are the two sums and the fp32 division.  The error of every
+    partial, relative to the largest product of its sums, must stay within
+    KAPPA_MFMA, the figure the FP8 tolerance (oracle.fp8) takes for the instruction.
+
+    Operand sets (one per chunk, rotating): random V of both signs; two keys
+    with equal scores and values +448 and -448, whose products cancel exactly,
+    over small random values (the sum is small beside its largest product, so
+    any bits the instruction drops below that product show); and values of
+    random sign spread from 2^-6 to 2^8."""
+    import torch
+    Tq, n_chunks, d = 64, 48, 128
+    Tk = 64 * n_chunks
+    rng = np.random.default_rng(77)
+    b = rng.choice([0.0, 1.0, -1.0], size=Tq)
+    x = -rng.integers(0, 4, size=Tk).astype(np.float64)
+    y = rng.choice([0.0, 1.0, -1.0], size=Tk)
+    v = np.empty((Tk, d))
+    for c in range(n_chunks):
+        blk = slice(64 * c, 64 * c + 64)
+        if c % 3 == 0:
+            v[blk] = rng.standard_normal((64, d)) * 60.0
+        elif c % 3 == 1:
+            v[blk] = rng.standard_normal((64, d))
+            v[64 * c] = 448.0
+            v[64 * c + 1] = -448.0
+            x[64 * c + 1], y[64 * c + 1] = x[64 * c], y[64 * c]     # the pair's scores are equal
+        else:
+            v[blk] = rng.choice([-1.0, 1.0], size=(64, d)) * np.exp2(rng.uniform(-6.0, 8.0, size=(64, d)))
+    v = np.clip(v, -448.0, 448.0).reshape(1, 1, Tk, d)
+    q = np.zeros((1, 1, Tq, d)); q[0, 0, :, 0] = 1.0; q[0, 0, :, 1] = b
+    k = np.zeros((1, 1, Tk, d)); k[0, 0, :, 0] = x; k[0, 0, :, 1] = y
+    q8, k8, v8 = (wl.f32_to_e4m3_bits(t.astype(np.float32)) for t in (q, k, v))
+    vf = ofp8.widen_e4m3(v8)[0, 0]
+    scale = float(np.float32(math.log(2.0)))
+    ws = torch.empty(fa.split_workspace_bytes(1, 1, Tq, Tk, d, n_chunks), dtype=torch.uint8, device="cuda:0")
+    o = torch.empty((1, 1, Tq, d), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((1, 1, Tq), device="cuda:0")
+    fa.fwd_fp8_out(to_dev8(q8), to_dev8(k8), to_dev8(v8), o, lse, False, scale, (1.0, 1.0, 1.0),
+                   n_split=n_chunks, workspace=ws)
+    torch.cuda.synchronize()
+    part = ws.view(torch.float32)[: n_chunks * Tq * d].view(n_chunks, Tq, d).cpu().numpy().astype(np.float64)
+    sc = (ofp8.widen_e4m3(k8)[0, 0] @ ofp8.widen_e4m3(q8)[0, 0].T).T          # (Tq, Tk) whole numbers
+    worst = np.zeros(3)
+    for c in range(n_chunks):
+        blk = slice(64 * c, 64 * c + 64)
+        s_c = sc[:, blk]
+        w = 8.0 * np.exp2(s_c - s_c.max(axis=1, keepdims=True))                # exact E4M3 weights
+        assert np.all(w >= 2.0 ** -6)
+        o_exact, l_exact = w @ vf[blk], w.sum(axis=1)
+        out = o_exact / l_exact[:, None]
+        scale_of_sums = np.max(np.abs(w[:, :, None] * vf[blk][None]), axis=1) + np.abs(out) * w.max(axis=1)[:, None]
+        err = np.abs(part[c] - out) * l_exact[:, None] - 2.0 ** -22 * np.abs(o_exact)
+        kappa = float(np.max(err / scale_of_sums))
+        worst[c % 3] = max(worst[c % 3], kappa)
+    say("FP8 instruction: largest partial error / largest product, by operand set "
+        f"(random, cancelling pair, spread): " + ", ".join(f"2^{math.log2(max(k_, 1e-30)):.2f}" for k_ in worst)
+        + f"; the tolerance takes 2^{math.log2(ofp8.KAPPA_MFMA):.0f}")
+    assert np.all(worst <= ofp8.KAPPA_MFMA), worst
 
 
 def test_split_workspace_reuse_and_stream(fa):
