@@ -73,6 +73,18 @@ def copy_probe(mib: int, dev) -> None:
     del src, dst
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (``/proc/cpuinfo``), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float, widened=None):
     """The oracle as it stands, on an evenly spaced row sample sized to ~target_s seconds.
     ``widened``: the float64 operands the oracle reads, when they are not bf16 bits."""
@@ -113,6 +125,7 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float, widened=None):
         "value": passes * row_flops(rows) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": ((f"all {n_rows_total} query rows (the whole workload), {passes} pass(es)"
                     if len(rows) == n_rows_total else
@@ -148,6 +161,7 @@ def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, dob, target_s: float):
         "value": passes * flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": ((f"the whole workload ({w.B * w.H} heads)" if whole else
                     f"{n_kv * g} of {w.B * w.H} query heads ({n_kv} key/value heads), every row")
