@@ -7,13 +7,15 @@ causal), a roofline object for the kernel (measured with HIP events on the
 launch stream) and a CPU-baseline object (the fp64 oracle timed on a bounded
 row sample on the host cores).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--pass fwd|bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--pass fwd|bwd] [--variant exp2poly]
 
 ``--workload c4fp8`` times the FP8 forward (``fa_fwd_fp8``) on the same shape
 with E4M3 inputs, against the fp8 MFMA peak.  ``--pass bwd`` times the backward instead (one step = one ``fa_bwd`` call: the
 per-row D pass, the dK/dV kernel and the dQ kernel), with O and lse from the
 forward computed before the timed region; its FLOP count is the usual 2.5x the
-forward's (five T x T x d products instead of two).
+forward's (five T x T x d products instead of two).  ``--variant exp2poly``
+times the forward built with part of its exponentials on the FMA path
+(``libfa_exp2poly.so``) on any bf16 workload.
 """
 from __future__ import annotations
 
@@ -30,19 +32,28 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from exact_io_aware_13_amd import build as hip_build  # noqa: E402
 from exact_io_aware_13_amd import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic_causal_b1h32t8192d128.json")
-
-
 FP8_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_fwd_fp8.hip")
-FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_traffic_causal_b1h32t8192d128.json")
 BWD_SRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc", "fa_bwd.hip")
-BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_traffic_causal_b1h32t8192d128.json")
+
+
+def profile_tag(w: wl.Workload) -> str:
+    """The workload's part of a profile file name, e.g. ``causal_b1h32t8192d128``."""
+    c = "causal" if w.causal else "noncausal"
+    if w.Hkv != w.H or w.Tk != w.T:
+        return f"{c}_b{w.B}hq{w.H}hkv{w.Hkv}tq{w.T}tk{w.Tk}d{w.d}"
+    return f"{c}_b{w.B}h{w.H}t{w.T}d{w.d}"
+
+
+def traffic_file(w: wl.Workload, kernel: str = "fa_fwd") -> str:
+    """The committed FETCH_SIZE/WRITE_SIZE figure for ``kernel`` on workload ``w``."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_traffic_{profile_tag(w)}.json")
 
 
 def kernel_hash(src: str = KERNEL_SRC) -> str:
@@ -50,7 +61,7 @@ def kernel_hash(src: str = KERNEL_SRC) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(key: str, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
+def measured_traffic(key: str, path: str, src: str = KERNEL_SRC):
     """HBM bytes per launch (per call) from the committed counter runs, if they match this kernel source."""
     try:
         with open(path) as f:
@@ -240,7 +251,7 @@ def bench_bwd(args, w: wl.Workload, dev) -> int:
         "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.key, BWD_TRAFFIC_FILE, BWD_SRC),
+                     "traffic": measured_traffic(w.key, traffic_file(w, "fa_bwd"), BWD_SRC),
                      "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": bwd_algorithmic_bytes(w),
                      "kernels": "fa_bwd_prep_kernel + fa_bwd_dkdv_kernel + fa_bwd_dq_kernel (one fa_bwd call)"},
     }
@@ -303,7 +314,7 @@ def bench_fp8(args, w: wl.Workload, dev) -> int:
         metric = f"attention fwd TFLOP/s and % of fp8 MFMA peak, {w.title}"
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                "traffic": measured_traffic(w.key, FP8_TRAFFIC_FILE, FP8_SRC),
+                "traffic": measured_traffic(w.key, traffic_file(w, "fa_fwd_fp8"), FP8_SRC),
                 "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": w.algorithmic_bytes()}
         config.update({"pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
                        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)})
@@ -344,6 +355,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
+    ap.add_argument("--variant", default=None, choices=sorted(hip_build.VARIANTS),
+                    help="time a measurement variant of the forward (libfa_<name>.so) instead of libfa.so")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one device copy of this size (counter calibration runs)")
     args = ap.parse_args(argv)
@@ -360,7 +373,10 @@ def main(argv=None) -> int:
     w = wl.BY_KEY[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    fa.load()
+    lib = fa.load(fa.variant_path(args.variant)) if args.variant else fa.load()
+    if args.variant and (args.pass_ == "bwd" or w.fp8):
+        print("--variant applies to the bf16 forward only", file=sys.stderr)
+        return 2
     if args.pass_ == "bwd":
         return bench_bwd(args, w, dev)
     if w.fp8:
@@ -375,12 +391,13 @@ def main(argv=None) -> int:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
     scale = float(np.float32(w.scale))
-    n_split = w.n_split if w.n_split is not None else fa.split_count(w.B, w.H, w.Hkv, w.T, w.Tk, w.d, w.causal)
-    ws_bytes = fa.split_workspace_bytes(w.B, w.H, w.T, w.Tk, w.d, n_split)
+    n_split = w.n_split if w.n_split is not None else fa.split_count(w.B, w.H, w.Hkv, w.T, w.Tk, w.d, w.causal,
+                                                                       lib)
+    ws_bytes = fa.split_workspace_bytes(w.B, w.H, w.T, w.Tk, w.d, n_split, lib)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step():
-        fa.fwd_out(q, k, v, o, lse, w.causal, scale, n_split=n_split, workspace=workspace)
+        fa.fwd_out(q, k, v, o, lse, w.causal, scale, n_split=n_split, workspace=workspace, lib=lib)
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
@@ -408,6 +425,8 @@ def main(argv=None) -> int:
 
     assert torch.isfinite(lse).all().item(), "non-finite lse"
 
+    # the committed counter figure is the product library's; a variant build has none
+    traffic = None if args.variant else measured_traffic(w.key, traffic_file(w))
     hbm_bound = w.algorithmic_bytes() * PEAK_BF16_TFLOPS * 1e12 > flops * PEAK_HBM_GBS * 1e9
     if w.key == wl.BENCH_KEY:
         metric = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal B=1 H=32 T=8192 d=128"
@@ -417,13 +436,13 @@ def main(argv=None) -> int:
         gbs = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
         value_out, unit = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9, "GB/s"
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.key),
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel_ms": round(kernel_ms, 4), "flops": flops}
     else:
         value_out, unit = value, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(w.key),
+                "traffic": traffic,
                 "kernel_ms": round(kernel_ms, 4),
                 "algorithmic_bytes": w.algorithmic_bytes()}
     config = {"workload": w.title, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "causal": w.causal}
@@ -431,6 +450,8 @@ def main(argv=None) -> int:
         config.update({"Hkv": w.Hkv, "Tk": w.Tk, "n_split": n_split})
     if not hbm_bound:
         config["pct_of_bf16_peak"] = round(100.0 * value / PEAK_BF16_TFLOPS, 2)
+    if args.variant:
+        config["variant"] = args.variant
     out = {
         "metric": metric,
         "value": round(value_out, 2),

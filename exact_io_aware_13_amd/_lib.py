@@ -29,7 +29,12 @@ SCRATCH_BYTES = 16 << 20      # FA_SCRATCH_BYTES: the fixed scratch of fa_fwd_sp
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_fwd_split_workspace_bytes", "fa_fwd_split_count",
             "fa_fwd_fp8", "fa_fwd_fp8_split", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string")
 
-_lib = None
+_libs = {}
+
+
+def variant_path(name: str) -> str:
+    """Path of a measurement variant of the library (``libfa_<name>.so``, built by ``build.build_all``)."""
+    return os.path.join(_PKG, f"libfa_{name}.so")
 
 
 class FAError(RuntimeError):
@@ -38,14 +43,15 @@ class FAError(RuntimeError):
         self.status = status
 
 
-def load() -> ctypes.CDLL:
-    """Load ``libfa.so`` (raises if it is missing)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() "
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load ``libfa.so``, or the library at ``path`` (a measurement variant with
+    the same C ABI); raises if it is missing."""
+    path = path or LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
                                "(or python exact_io_aware_13_amd/build.py) first")
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, vp]
         lib.fa_fwd.restype = ctypes.c_int
@@ -77,34 +83,35 @@ def load() -> ctypes.CDLL:
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_hip_error_string.argtypes = []
         lib.fa_hip_error_string.restype = ctypes.c_char_p
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
 
 
-def status_string(status: int) -> str:
-    return load().fa_status_string(int(status)).decode()
+def status_string(status: int, lib: ctypes.CDLL | None = None) -> str:
+    return (lib or load()).fa_status_string(int(status)).decode()
 
 
 def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
-               B: int, H: int, T: int, d: int, causal: int, scale: float, stream: int) -> int:
+               B: int, H: int, T: int, d: int, causal: int, scale: float, stream: int,
+               lib: ctypes.CDLL | None = None) -> int:
     """Call ``fa_fwd`` with raw addresses; returns the fa_status code."""
-    return int(load().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, T, d, int(causal),
-                             float(scale), stream))
+    return int((lib or load()).fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, T, d, int(causal),
+                                      float(scale), stream))
 
 
 def fa_fwd_gqa_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
-                   T: int, d: int, causal: int, scale: float, stream: int) -> int:
+                   T: int, d: int, causal: int, scale: float, stream: int, lib: ctypes.CDLL | None = None) -> int:
     """Call ``fa_fwd_gqa`` with raw addresses; returns the fa_status code."""
-    return int(load().fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, T, d, int(causal),
-                                 float(scale), stream))
+    return int((lib or load()).fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, T, d, int(causal),
+                                          float(scale), stream))
 
 
 def fa_fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
                      Tq: int, Tk: int, d: int, causal: int, scale: float, n_split: int, ws_ptr: int,
-                     ws_bytes: int, stream: int) -> int:
+                     ws_bytes: int, stream: int, lib: ctypes.CDLL | None = None) -> int:
     """Call ``fa_fwd_split`` with raw addresses; returns the fa_status code."""
-    return int(load().fa_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d, int(causal),
-                                   float(scale), n_split, ws_ptr, ws_bytes, stream))
+    return int((lib or load()).fa_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Tq, Tk, d,
+                                            int(causal), float(scale), n_split, ws_ptr, ws_bytes, stream))
 
 
 def fa_fwd_split_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int,
@@ -115,12 +122,14 @@ def fa_fwd_split_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse
                                            int(causal), float(scale), int(n_split), stream))
 
 
-def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: int) -> int:
-    return int(load().fa_fwd_split_workspace_bytes(B, Hq, Tq, Tk, d, n_split))
+def split_workspace_bytes(B: int, Hq: int, Tq: int, Tk: int, d: int, n_split: int,
+                          lib: ctypes.CDLL | None = None) -> int:
+    return int((lib or load()).fa_fwd_split_workspace_bytes(B, Hq, Tq, Tk, d, n_split))
 
 
-def split_count(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: bool) -> int:
-    return int(load().fa_fwd_split_count(B, Hq, Hkv, Tq, Tk, d, int(bool(causal))))
+def split_count(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, d: int, causal: bool,
+                lib: ctypes.CDLL | None = None) -> int:
+    return int((lib or load()).fa_fwd_split_count(B, Hq, Hkv, Tq, Tk, d, int(bool(causal))))
 
 
 def fa_fwd_fp8_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, Hq: int, Hkv: int,
@@ -152,11 +161,11 @@ def bwd_workspace_bytes(B: int, Hq: int, Tq: int) -> int:
     return int(load().fa_bwd_workspace_bytes(B, Hq, Tq))
 
 
-def _check(status: int, entry: str = "fa_fwd") -> None:
+def _check(status: int, entry: str = "fa_fwd", lib: ctypes.CDLL | None = None) -> None:
     if status != FA_OK:
-        msg = status_string(status)
+        msg = status_string(status, lib)
         if status == FA_ERR_HIP:
-            msg += f" ({load().fa_hip_error_string().decode()})"
+            msg += f" ({(lib or load()).fa_hip_error_string().decode()})"
         raise FAError(status, msg, entry)
 
 
@@ -191,7 +200,7 @@ def _check_workspace(workspace, device) -> None:
 
 
 def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: int | None = 1,
-            workspace=None) -> None:
+            workspace=None, lib: ctypes.CDLL | None = None) -> None:
     """Exact attention forward into caller buffers ``o`` (bf16, like q) and ``lse`` (fp32, (B, Hq, Tq)).
 
     ``q``: (B, Hq, Tq, d); ``k, v``: (B, Hkv, Tk, d).  One key/value head per
@@ -199,7 +208,8 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
     ``fa_fwd_gqa``; anything else (Tq != Tk, or ``n_split`` != 1; ``None`` asks
     the library for a split count) calls ``fa_fwd_split``.  A split forward
     needs ``workspace`` (a uint8 GPU tensor of ``split_workspace_bytes`` bytes);
-    if it is not given, one is allocated here.
+    if it is not given, one is allocated here.  ``lib``: a library from
+    ``load(path)`` (a measurement variant) instead of ``libfa.so``.
     """
     import torch
     _check_tensors(q, k, v)
@@ -212,18 +222,18 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if n_split is None:
-        n_split = split_count(B, Hq, Hkv, Tq, Tk, d, causal)
+        n_split = split_count(B, Hq, Hkv, Tq, Tk, d, causal, lib)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         if Tq == Tk and n_split == 1:
             if Hkv == Hq:
                 st = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                B, Hq, Tq, d, int(bool(causal)), float(scale), stream)
+                                B, Hq, Tq, d, int(bool(causal)), float(scale), stream, lib)
             else:
                 st = fa_fwd_gqa_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                    B, Hq, Hkv, Tq, d, int(bool(causal)), float(scale), stream)
+                                    B, Hq, Hkv, Tq, d, int(bool(causal)), float(scale), stream, lib)
         else:
-            need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split)
+            need = split_workspace_bytes(B, Hq, Tq, Tk, d, n_split, lib)
             if workspace is None and need > 0:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             elif workspace is not None:
@@ -232,8 +242,8 @@ def fwd_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: 
             ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
             st = fa_fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), int(n_split),
-                                  ws_ptr, ws_bytes, stream)
-        _check(st)
+                                  ws_ptr, ws_bytes, stream, lib)
+        _check(st, "fa_fwd", lib)
 
 
 def fwd_noalloc_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n_split: int | None = None) -> None:
@@ -260,21 +270,22 @@ def fwd_noalloc_out(q, k, v, o, lse, causal: bool, scale: float | None = None, n
     _check(st, "fa_fwd_split_noalloc")
 
 
-def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None = 1):
+def fwd(q, k, v, causal: bool, scale: float | None = None, n_split: int | None = 1,
+        lib: ctypes.CDLL | None = None):
     """Exact attention forward; returns ``(o, lse)``.
 
     ``q``: contiguous bf16 GPU tensor (B, Hq, Tq, d); ``k, v``: (B, Hkv, Tk, d),
     d in {64, 128}, Hq a multiple of Hkv.  ``scale`` defaults to 1/sqrt(d).
     With ``causal`` the queries are the last Tq positions (query i sees keys
     j <= i + Tk - Tq).  ``o`` is bf16 like ``q``; ``lse`` is float32
-    (B, Hq, Tq) in natural-log units.  ``n_split`` as in ``fwd_out``.
+    (B, Hq, Tq) in natural-log units.  ``n_split`` and ``lib`` as in ``fwd_out``.
     """
     import torch
     _check_tensors(q, k, v)
     B, Hq, Tq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
-    fwd_out(q, k, v, o, lse, causal, scale, n_split)
+    fwd_out(q, k, v, o, lse, causal, scale, n_split, lib=lib)
     return o, lse
 
 

@@ -21,6 +21,15 @@ SRCS = [os.path.join(PKG, "csrc", "fa_fwd.hip"), os.path.join(PKG, "csrc", "fa_b
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
+# Measurement variants: the same sources built with one compile-time choice
+# changed, each a library of its own with the same C ABI.  ``exp2poly`` takes
+# 4 of every 32 forward weights from the polynomial 2^x (``kPolyExp2`` in
+# fa_fwd.hip) at both head sizes.
+VARIANTS = {"exp2poly": ["-DFA_EXP2_POLY=4"]}
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(PKG, f"libfa_{name}.so")
 
 
 def hipcc() -> str:
@@ -57,5 +66,14 @@ def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = 
     return out
 
 
+def build_all(force: bool = True, quiet: bool = True) -> list:
+    """Build ``libfa.so`` and every measurement variant; returns their paths."""
+    out = [build(force=force, quiet=quiet)]
+    for name, flags in VARIANTS.items():
+        out.append(build(force=force, extra=flags, out=variant_path(name), quiet=quiet))
+    return out
+
+
 if __name__ == "__main__":
-    print(build(force=True, quiet=False))
+    for path in build_all(force=True, quiet=False):
+        print(path)

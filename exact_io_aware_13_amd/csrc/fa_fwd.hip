@@ -157,6 +157,39 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
     return xhalf_max(fmaxf(max3f(b0, b1, b2), b3));
 }
 
+// FA4's polynomial exponential ("FlashAttention and Fused Kernels", "Four
+// generations of FlashAttention"): a share of the weights is computed on the
+// FMA path instead of the transcendental unit.  kPolyExp2<D> is how many of a
+// lane's 32 weights per key tile take it, per head size.  On gfx950 the
+// transcendental instruction issues through the same VALU port as the FMAs,
+// and the polynomial costs eight VALU instructions where v_exp_f32 costs one,
+// so no head size takes it; building with FA_EXP2_POLY=n gives n at every
+// head size, the variant that measures the trade.
+#ifdef FA_EXP2_POLY
+template <int D>
+constexpr int kPolyExp2 = FA_EXP2_POLY;
+#else
+template <int D>
+constexpr int kPolyExp2 = 0;
+#endif
+static_assert(kPolyExp2<64> >= 0 && kPolyExp2<64> <= 32 && (kPolyExp2<64> == 0 || 32 % kPolyExp2<64> == 0));
+static_assert(kPolyExp2<128> >= 0 && kPolyExp2<128> <= 32 && (kPolyExp2<128> == 0 || 32 % kPolyExp2<128> == 0));
+
+// 2^x as 2^floor(x) * q(frac(x)), q the cubic with q(0) = 1 that minimises the
+// largest relative error against 2^f on [0, 1) (fitted by iteratively
+// reweighted least squares on [0, 1]: 9.5e-5).  x is first clamped to [-160, 128], so
+// masked scores (-inf) give exactly 0 and overflow gives +inf, as v_exp_f32.
+__device__ __forceinline__ float exp2_poly(float x) {
+    const float y = __builtin_amdgcn_fmed3f(x, -160.0f, 128.0f);
+    const float fl = __builtin_floorf(y);
+    const float f = y - fl;          // in [0, 1]: 1 only where y is just below an integer, and q(1) ~ 2
+    const int e = static_cast<int>(fl);
+    float q = __builtin_fmaf(f, 0.07714322f, 0.22765102f);
+    q = __builtin_fmaf(f, q, 0.69507057f);
+    q = __builtin_fmaf(f, q, 1.0f);
+    return __builtin_amdgcn_ldexpf(q, e);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2 v;
     v[0] = static_cast<__bf16>(a);
@@ -444,8 +477,11 @@ __device__ __forceinline__ void fa_fwd_block(const uint16_t* __restrict__ Q, con
         auto weights = [&] __device__ () {
             const float mneg = -st.m;
 #pragma unroll
-            for (int n = 0; n < 32; ++n)
-                p[n] = __builtin_amdgcn_exp2f(__builtin_fmaf(n < 16 ? sc[0][n] : sc[1][n - 16], c, mneg));
+            for (int n = 0; n < 32; ++n) {
+                const float x = __builtin_fmaf(n < 16 ? sc[0][n] : sc[1][n - 16], c, mneg);
+                constexpr int kEvery = kPolyExp2<D> ? 32 / kPolyExp2<D> : 0;
+                p[n] = kEvery && n % kEvery == 0 ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
+            }
             float t8[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) t8[q] = (p[4 * q] + p[4 * q + 1]) + (p[4 * q + 2] + p[4 * q + 3]);

@@ -11,6 +11,7 @@ import subprocess
 import pytest
 
 from exact_io_aware_13_amd import _lib
+from exact_io_aware_13_amd import build as build_mod
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -44,6 +45,22 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
+
+
+@pytest.mark.parametrize("name", sorted(build_mod.VARIANTS))
+def test_variant_library_exports_every_declared_symbol(name):
+    """Each measurement variant is the same C ABI built with one compile-time choice changed."""
+    path = _lib.variant_path(name)
+    assert path == build_mod.variant_path(name)
+    if not os.path.exists(path):
+        build_mod.build(force=True, extra=build_mod.VARIANTS[name], out=path)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert _declared_functions() <= exported
+    vlib = _lib.load(path)
+    assert vlib is not _lib.load() and vlib is _lib.load(path)
+    assert _lib.status_string(0, vlib) == _lib.status_string(0)
 
 
 def test_status_strings(lib):

@@ -43,6 +43,26 @@ def test_traffic_figure_is_keyed_to_the_kernel_source(tmp_path):
     assert bench.measured_traffic("c4", str(tmp_path / "missing.json"), str(src)) is None
 
 
+def test_traffic_files_are_named_by_workload_shape():
+    assert bench.traffic_file(wl.BY_KEY["c4"]).endswith("profiles/fa_fwd_traffic_causal_b1h32t8192d128.json")
+    assert bench.traffic_file(wl.BY_KEY["c3nc"]).endswith("fa_fwd_traffic_noncausal_b16h16t1024d64.json")
+    assert bench.traffic_file(wl.BY_KEY["c4fp8"], "fa_fwd_fp8").endswith(
+        "fa_fwd_fp8_traffic_causal_b1h32t8192d128.json")
+    assert bench.profile_tag(wl.BY_KEY["decode"]) == "causal_b8hq32hkv8tq1tk32768d128"
+    # every committed traffic figure names the workload its file name says
+    for w in wl.WORKLOADS:
+        for kernel in ("fa_fwd", "fa_fwd_fp8", "fa_bwd"):
+            path = bench.traffic_file(w, kernel)
+            if os.path.exists(path) and w.fp8 == (kernel == "fa_fwd_fp8"):
+                with open(path) as f:
+                    assert json.load(f)["workload"] == w.key, path
+
+
+def test_variant_names_come_from_the_build():
+    with pytest.raises(SystemExit):
+        bench.main(["--variant", "nosuch"])
+
+
 def test_cpu_baseline_object_on_the_small_workload():
     w = wl.BY_KEY["c1"]
     qb, kb, vb = wl.workload_inputs(w)

@@ -47,6 +47,20 @@ def test_no_register_spills(asm):
     assert spills and max(spills) == 0 and max(sgpr_spills) == 0
 
 
+@pytest.mark.parametrize("name", sorted(build.VARIANTS))
+def test_measurement_variants_compile_every_kernel_without_spills(name, tmp_path):
+    out = tmp_path / f"fa_fwd_{name}.s"
+    cmd = [build.hipcc()] + [f for f in build.compile_flags() if f != "-fPIC"] + build.VARIANTS[name] + \
+        ["--cuda-device-only", "-S", "-o", str(out), build.SRCS[0]]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = out.read_text()
+    assert len(list(_kernels(text))) == 16
+    spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
+    assert spills and max(spills) == 0
+    if name == "exp2poly":      # the polynomial's scaling step is there, and so is v_exp_f32
+        assert "v_ldexp_f32" in text and "v_exp_f32" in text
+
+
 def test_lds_reads_do_not_wait_on_tile_loads(asm):
     for name, body in _kernels(asm):
         waits = [i for i, (a, b) in enumerate(zip(body, body[1:]))
