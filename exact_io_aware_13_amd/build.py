@@ -66,11 +66,33 @@ def build(force: bool = True, extra=None, out: str | None = None, quiet: bool = 
     return out
 
 
+C_CLIENT_SRC = os.path.join(PKG, "csrc", "fa_c_client.c")
+C_CLIENT = os.path.join(PKG, "fa_c_client")
+
+
+def build_c_client(force: bool = True) -> str:
+    """Compile ``fa_c_client``, a plain C program that calls ``libfa.so`` through
+    ``include/fa.h`` (gcc, linked against the library beside it)."""
+    if not force and os.path.exists(C_CLIENT) and os.path.getmtime(C_CLIENT) >= max(
+            os.path.getmtime(C_CLIENT_SRC), os.path.getmtime(LIB)):
+        return C_CLIENT
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), C_CLIENT_SRC, "-L", PKG, "-lfa", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", C_CLIENT + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    os.replace(C_CLIENT + ".tmp", C_CLIENT)
+    return C_CLIENT
+
+
 def build_all(force: bool = True, quiet: bool = True) -> list:
-    """Build ``libfa.so`` and every measurement variant; returns their paths."""
+    """Build ``libfa.so``, every measurement variant and the C client; returns their paths."""
     out = [build(force=force, quiet=quiet)]
     for name, flags in VARIANTS.items():
         out.append(build(force=force, extra=flags, out=variant_path(name), quiet=quiet))
+    out.append(build_c_client(force=force))
     return out
 
 

@@ -339,3 +339,14 @@ def test_binding_rejects_bad_workspace():
         _lib._check_workspace(ok, torch.device("cuda", 0))
     with pytest.raises(ValueError):
         _lib._check_workspace(torch.empty(8, 8, dtype=torch.uint8).t(), ok.device)
+
+
+def test_c_client_is_built_against_the_library():
+    """The plain C client links libfa.so (found beside it) and the HIP runtime."""
+    from exact_io_aware_13_amd import build as b
+    if not os.path.exists(b.C_CLIENT):
+        b.build_c_client(force=True)
+    out = subprocess.run(["ldd", b.C_CLIENT], capture_output=True, text=True, check=True).stdout
+    assert os.path.join(os.path.dirname(b.C_CLIENT), "libfa.so") in out or "libfa.so =>" in out
+    assert "libamdhip64" in out
+    assert "fa_fwd_split" in open(b.C_CLIENT_SRC).read()
