@@ -1,0 +1,54 @@
+"""The library's host code under AddressSanitizer (no GPU needed).
+
+A copy of libfa.so is built with the host pass instrumented (each sanitizer
+flag behind ``-Xarch_host``, so no device code is), and the host-side ABI tests
+(argument validation, status strings, overlap and workspace checks, the
+allocation-free entry point's checks) run against it in a child process with
+the sanitizer runtime preloaded.  Any out-of-bounds access or use after free in
+those paths fails the test."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from exact_io_aware_13_amd import build as hip_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _asan_runtime():
+    for clang in ("/opt/rocm/llvm/bin/clang", "clang"):
+        try:
+            out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                                 text=True, timeout=60).stdout.strip()
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if out and os.path.isabs(out) and os.path.exists(out):
+            return out
+    return None
+
+
+def test_host_abi_paths_are_clean_under_asan(tmp_path):
+    rt = _asan_runtime()
+    if rt is None:
+        pytest.skip("no AddressSanitizer runtime for the ROCm clang")
+    lib = tmp_path / "libfa_asan.so"
+    flags = [f for f in hip_build.compile_flags() if f != "-O3"] + ["-O1", "-g"]
+    flags += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    cmd = [hip_build.hipcc()] + flags + ["-shared", "-o", str(lib)] + hip_build.SRCS
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    driver = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from exact_io_aware_13_amd import _lib\n"
+        "_lib.LIB_PATH = %r\n"
+        "import pytest\n"
+        "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r, '-k', "
+        "'not variant and not c_client and not exports']))\n" % (ROOT, str(lib), os.path.join(ROOT, "tests", "test_abi_host.py")))
+    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0")
+    run = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True, env=env, timeout=600)
+    out = run.stdout + run.stderr
+    assert "AddressSanitizer" not in out, out[-4000:]
+    assert run.returncode == 0, out[-4000:]
+    assert " passed" in out
