@@ -171,7 +171,8 @@ E4M3_MAX = 448.0
 def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     """Round values to OCP FP8 E4M3 (round to nearest, ties to even), saturating
     at +-448; returns uint8 bits (sign, 4 exponent bits with bias 7, 3 mantissa
-    bits; exponent field 0 holds the subnormals m * 2^-9)."""
+    bits; exponent field 0 holds the subnormals m * 2^-9).  The sign is kept,
+    also where the value rounds to zero (-0 is 0x80), as IEEE rounding does."""
     x = np.asarray(x, dtype=np.float64)
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite input values")
@@ -186,7 +187,7 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     m_sub = np.rint(r / 2.0 ** -9)
     m_nrm = np.rint(r / np.exp2(e2) * 8.0) - 8.0
     bits = np.where(sub, m_sub, (e2 + 7.0) * 8.0 + m_nrm).astype(np.uint8)
-    return bits | np.where(np.signbit(x) & (r > 0), np.uint8(0x80), np.uint8(0))
+    return bits | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
 
 
 def e4m3_descale(x: np.ndarray) -> np.float32:

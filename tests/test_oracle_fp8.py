@@ -282,3 +282,25 @@ def test_attention_fp8_rows_match_full():
     orow, lrow = ofp8.attention_fp8_rows_f64(q, k, v, ds, True, 0.3, rows)
     assert np.abs(orow - o.reshape(-1, 8)[rows]).max() <= 1e-13
     assert np.abs(lrow - lse.reshape(-1)[rows]).max() <= 1e-13
+
+
+def test_decoder_and_encoder_match_torch_float8_e4m3fn():
+    """Library pin: torch's float8_e4m3fn (the OCP E4M3 format) decodes every
+    code as the oracle does, and rounds in-range fp32 values to the same codes."""
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ofp8.widen_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and int(nan.sum()) == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    rng = np.random.default_rng(11)
+    table = got[:0x7F]
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * 60, rng.standard_normal(5000).astype(np.float32)
+                        * np.float32(2.0 ** -8), ((table[1:] + table[:-1]) / 2).astype(np.float32)])
+    x = x[np.abs(x) <= 448].astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(wl.f32_to_e4m3_bits(x), want)
