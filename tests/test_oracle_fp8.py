@@ -304,3 +304,27 @@ def test_decoder_and_encoder_match_torch_float8_e4m3fn():
     x = x[np.abs(x) <= 448].astype(np.float32)
     want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(wl.f32_to_e4m3_bits(x), want)
+
+
+def test_attention_fp8_matches_torch_on_torch_decoded_operands():
+    """Library pin of the whole FP8 oracle: torch decodes the E4M3 bytes
+    (float8_e4m3fn), applies the fp32 descales, and its float64
+    scaled_dot_product_attention gives the oracle's O, causal and not."""
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(12)
+    B, H, T, d = 1, 2, 37, 16
+    q8, k8, v8 = (wl.f32_to_e4m3_bits(rng.standard_normal((B, H, T, d)) * 30) for _ in range(3))
+    ds = (np.float32(0.05), np.float32(0.03), np.float32(0.2))
+    scale = 1.0 / math.sqrt(d)
+
+    def torch_dq(b, s):
+        return torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64) * float(s)
+
+    for causal in (False, True):
+        o, lse = ofp8.attention_fp8_f64(q8, k8, v8, ds, causal, scale)
+        ref = F.scaled_dot_product_attention(torch_dq(q8, ds[0]), torch_dq(k8, ds[1]), torch_dq(v8, ds[2]),
+                                             is_causal=causal, scale=scale).numpy()
+        assert np.abs(o - ref).max() <= 1e-12
