@@ -140,6 +140,43 @@ def test_every_row(fa, case):
     check8(o, lse, q8, k8, v8, ds, causal, scale, all_rows(q8), f"fp8 {case}")
 
 
+def _random_fp8_cases(n, seed):
+    """Seeded shapes: batch 1-2, 1-2 key/value heads each shared by 1, 2 or 4
+    query heads, lengths 1-1600 (causal only where Tq <= Tk), both head sizes,
+    scales within 2/sqrt(d), and one or several key splits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        Tk = int(rng.choice([int(rng.integers(1, 100)), int(rng.integers(100, 1600))]))
+        Tq = Tk if rng.random() < 0.6 else int(rng.integers(1, 1600))
+        causal = bool(rng.random() < 0.6) and Tq <= Tk
+        scale = float(np.float32(rng.choice([1.0, 0.5, 2.0, -1.0]) / math.sqrt(d)))
+        n_split = int(rng.choice([1, 1, 2, 3, 5]))
+        out.append((int(rng.integers(1, 3)), Hq, Hkv, Tq, Tk, d, causal, scale, n_split))
+    return out
+
+
+RANDOM8 = _random_fp8_cases(16, 8008)
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM8)))
+def test_random_shapes_every_row(fa, case):
+    """Seeded random shapes through fa_fwd_fp8 and fa_fwd_fp8_split, every row
+    against the oracle within the derived per-element bound."""
+    import torch
+    B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split = RANDOM8[case]
+    label = f"fp8 random B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} causal={causal} scale={scale:.4g} splits={n_split}"
+    say("case", label)
+    q8, k8, v8, ds = draw8((B, Hq, Tq, d), (B, Hkv, Tk, d), seed=3000 + case)
+    o, lse = fa.fwd_fp8(to_dev8(q8), to_dev8(k8), to_dev8(v8), causal, scale, ds, n_split=n_split)
+    torch.cuda.synchronize()
+    o = oracle.widen_bf16(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    check8(o, lse.cpu().numpy().astype(np.float64), q8, k8, v8, ds, causal, np.float32(scale), all_rows(q8), label)
+
+
 # Long rows: the 8-wave workgroup shape (T >= 8192 causal, >= 4096 unmasked), a
 # spiky draw (row scales x8 force rescales), on sampled rows.
 LONG = [((1, 2, 2, 8292, 8292, 128, True), False), ((1, 2, 2, 4200, 4200, 128, False), False),
