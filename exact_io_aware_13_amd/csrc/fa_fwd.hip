@@ -913,8 +913,8 @@ extern "C" fa_status fa_fwd_split_noalloc(const void* q, const void* k, const vo
     return run_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, n_split, nullptr, 0, stream, true);
 }
 
-extern "C" const char* fa_status_string(fa_status status) {
-    switch (status) {
+extern "C" const char* fa_status_string(int status) {
+    switch (status) {   // an int: a C caller may pass any value, and only the listed ones are fa_status values
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "sizes must be >= 1, Hq a multiple of Hkv, and Tq <= Tk when causal";

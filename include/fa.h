@@ -294,8 +294,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 /* Workspace bytes fa_bwd needs: 8 per query row (0 for invalid sizes). */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq);
 
-/* Static, human-readable text for a status code (never NULL). */
-const char* fa_status_string(fa_status status);
+/* Static, human-readable text for a status code (never NULL).  status is an
+ * fa_status value; any other int gives "unknown status". */
+const char* fa_status_string(int status);
 
 /* Text of the HIP error of the calling thread's last call of any entry point
  * above, or "" when that call launched successfully */

@@ -1,11 +1,13 @@
-"""The library's host code under AddressSanitizer (no GPU needed).
+"""The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer
+(no GPU needed).
 
 A copy of libfa.so is built with the host pass instrumented (each sanitizer
 flag behind ``-Xarch_host``, so no device code is), and the host-side ABI tests
 (argument validation, status strings, overlap and workspace checks, the
 allocation-free entry point's checks) run against it in a child process with
-the sanitizer runtime preloaded.  Any out-of-bounds access or use after free in
-those paths fails the test."""
+the sanitizer runtime preloaded.  Any out-of-bounds access, use after free or
+undefined behaviour (signed overflow, invalid enum values, misaligned access,
+...) in those paths fails the test."""
 import os
 import subprocess
 import sys
@@ -29,13 +31,14 @@ def _asan_runtime():
     return None
 
 
-def test_host_abi_paths_are_clean_under_asan(tmp_path):
+def test_host_abi_paths_are_clean_under_sanitizers(tmp_path):
     rt = _asan_runtime()
     if rt is None:
         pytest.skip("no AddressSanitizer runtime for the ROCm clang")
-    lib = tmp_path / "libfa_asan.so"
+    lib = tmp_path / "libfa_sanitized.so"
     flags = [f for f in hip_build.compile_flags() if f != "-O3"] + ["-O1", "-g"]
-    flags += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags += ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+              "-Xarch_host", "-fno-omit-frame-pointer"]
     cmd = [hip_build.hipcc()] + flags + ["-shared", "-o", str(lib)] + hip_build.SRCS
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
@@ -46,9 +49,10 @@ def test_host_abi_paths_are_clean_under_asan(tmp_path):
         "import pytest\n"
         "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r, '-k', "
         "'not variant and not c_client and not exports']))\n" % (ROOT, str(lib), os.path.join(ROOT, "tests", "test_abi_host.py")))
-    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0")
+    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     run = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True, env=env, timeout=600)
     out = run.stdout + run.stderr
-    assert "AddressSanitizer" not in out, out[-4000:]
+    assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert run.returncode == 0, out[-4000:]
     assert " passed" in out
