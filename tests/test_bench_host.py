@@ -70,3 +70,16 @@ def test_cpu_baseline_object_on_the_small_workload():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["cores"] >= 1 and np.isfinite(r["value"]) and r["value"] > 0
     assert "query rows" in r["sample"]
+
+
+def test_committed_traffic_matches_the_current_kernel_sources():
+    """The headline workload and the profiled companions carry a traffic figure:
+    their committed counter runs were taken on the sources as they stand (a
+    kernel source edited without new counter runs makes ``traffic`` null)."""
+    cases = [("c4", "fa_fwd", bench.KERNEL_SRC), ("c2", "fa_fwd", bench.KERNEL_SRC),
+             ("c3c", "fa_fwd", bench.KERNEL_SRC), ("c3nc", "fa_fwd", bench.KERNEL_SRC),
+             ("c4fp8", "fa_fwd_fp8", bench.FP8_SRC), ("c4", "fa_bwd", bench.BWD_SRC)]
+    for key, kernel, src in cases:
+        path = bench.traffic_file(wl.BY_KEY[key], kernel)
+        got = bench.measured_traffic(key, path, src)
+        assert got is not None and got > wl.BY_KEY[key].algorithmic_bytes() * 0.9, (key, kernel, path)
