@@ -42,16 +42,19 @@ def test_host_abi_paths_are_clean_under_sanitizers(tmp_path):
     cmd = [hip_build.hipcc()] + flags + ["-shared", "-o", str(lib)] + hip_build.SRCS
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    driver = (
+    script = (
         "import sys; sys.path.insert(0, %r)\n"
         "from exact_io_aware_13_amd import _lib\n"
         "_lib.LIB_PATH = %r\n"
         "import pytest\n"
         "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r, '-k', "
         "'not variant and not c_client and not exports']))\n" % (ROOT, str(lib), os.path.join(ROOT, "tests", "test_abi_host.py")))
-    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0",
+    # The sanitizer runtime must come first among the preloaded libraries; anything
+    # already preloaded in this environment stays, after it.
+    preload = ":".join(x for x in (rt, os.environ.get("LD_PRELOAD", "")) if x)
+    env = dict(os.environ, LD_PRELOAD=preload, ASAN_OPTIONS="detect_leaks=0",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
-    run = subprocess.run([sys.executable, "-c", driver], capture_output=True, text=True, env=env, timeout=600)
+    run = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, env=env, timeout=600)
     out = run.stdout + run.stderr
     assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert run.returncode == 0, out[-4000:]
